@@ -1,0 +1,283 @@
+"""Pins for the CPU oracle: each test checks it against something other than itself.
+
+All of these run on the CPU (no GPU marker).  A plausible mistake in the
+oracle -- a dropped term, a wrong sign, a swapped nibble, a transposed
+operand, a wrong scale index -- fails at least one of them.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- codebook
+
+def test_codebook_matches_quantile_construction():
+    """The literal table equals the QLoRA quantile construction to fp32 precision."""
+    built = oracle.codebook_from_quantiles()
+    diff = np.max(np.abs(oracle.NF4_LEVELS.astype(np.float64) - built))
+    assert diff <= 5e-7, diff
+
+
+def test_codebook_fixed_points_and_order():
+    q = oracle.NF4_LEVELS
+    assert q.dtype == np.float32 and q.shape == (16,)
+    assert q[0] == -1.0 and q[7] == 0.0 and q[15] == 1.0
+    assert np.all(np.diff(q.astype(np.float64)) > 0)
+    assert np.sum(q < 0) == 7 and np.sum(q > 0) == 8
+
+
+def test_num_k_blocks_page_value():
+    with open(os.path.join(GOLDEN, "page_shapes.json")) as f:
+        gold = json.load(f)
+    for K, nb in gold["num_k_blocks"]:
+        assert oracle.num_k_blocks(K) == nb
+
+
+# ----------------------------------------------------------- layout / unpack
+
+def _layout_example():
+    with open(os.path.join(GOLDEN, "nibble_layout_example.json")) as f:
+        gold = json.load(f)
+    N, K = gold["N"], gold["K"]
+    flat = np.full(N * K // 2, gold["bytes_default"], dtype=np.uint8)
+    for idx, val in gold["bytes_set"].items():
+        flat[int(idx)] = val
+    return gold, N, K, flat.reshape(N, K // 2)
+
+
+def test_unpack_matches_hand_worked_addressing():
+    gold, N, K, b = _layout_example()
+    codes = oracle.unpack_codes(b, N, K)
+    for key, want in gold["expected_codes_at"].items():
+        n, k = key.split("_")
+        assert codes[int(n[1:]), int(k[1:])] == want, key
+
+
+def test_pack_codes_inverts_unpack():
+    b = synth.random_code_bytes(5, 192, seed=3)
+    assert np.array_equal(oracle.pack_codes(oracle.unpack_codes(b, 5, 192)), b)
+
+
+def test_dequant_nibble_order_probe():
+    """Even-k nibble 15 and odd-k nibble 7 dequantise to s, 0, s, 0, ..."""
+    N, K = 3, 128
+    b = np.full((N, K // 2), 0x7F, dtype=np.uint8)
+    s = np.array([[0.5, 2.0], [4.0, 0.25], [1.0, 8.0]], dtype=np.float32)
+    w = oracle.dequant(s, b, N, K)
+    for n in range(N):
+        for k in range(K):
+            want = s[n, k // 64] if k % 2 == 0 else 0.0
+            assert w[n, k] == want
+
+
+def test_dequant_scale_index_probe():
+    """Distinct power-of-two scales per (n, block) with all codes 15 reveal the scale map."""
+    N, K = 4, 256
+    s = np.array([[2.0 ** (n * 4 + kb - 8) for kb in range(4)] for n in range(N)], dtype=np.float32)
+    b = np.full((N, K // 2), 0xFF, dtype=np.uint8)
+    w = oracle.dequant(s, b, N, K)
+    for n in range(N):
+        for k in range(K):
+            assert w[n, k] == 2.0 ** (n * 4 + k // 64 - 8)
+
+
+def test_dequant_is_one_fp32_multiply():
+    """Bit-identical to an IEEE fp32 multiply done in float32 arithmetic."""
+    N, K = 37, 320
+    b = synth.random_code_bytes(N, K, seed=11)
+    s = synth.random_scales_uniform(N, K, seed=12, lo=1e-3, hi=3.0)
+    w = oracle.dequant(s, b, N, K)
+    codes = np.empty((N, K), dtype=np.int64)
+    for n in range(N):                      # independent unpack: Python integer ops per byte
+        for i in range(K // 2):
+            v = int(b[n, i])
+            codes[n, 2 * i] = v % 16
+            codes[n, 2 * i + 1] = v // 16
+    q32 = oracle.NF4_LEVELS[codes]
+    s32 = np.repeat(s, 64, axis=1)
+    with np.errstate(all="raise"):
+        direct = np.multiply(s32, q32, dtype=np.float32)
+    assert np.array_equal(w.view(np.uint32), direct.view(np.uint32))
+
+
+# ----------------------------------------------------------------- grad_A
+
+@pytest.mark.parametrize("M,N,K,seed", [(1, 1, 64, 0), (3, 5, 64, 1), (4, 17, 128, 2), (2, 33, 192, 3)])
+def test_grad_a_matches_fsum_bruteforce(M, N, K, seed):
+    b = synth.random_code_bytes(N, K, seed)
+    s = synth.random_scales_uniform(N, K, seed + 100)
+    g = synth.grad_out_normal(M, N, seed + 200)
+    ref, S = oracle.grad_a(g, s, b, M, N, K)
+    w = oracle.dequant(s, b, N, K)
+    exact = oracle.grad_a_bruteforce(g, w)
+    assert np.all(np.abs(ref - exact) <= 1e-12 * S + 1e-300)
+    # S itself: brute-force sum of absolute products
+    S_bf = oracle.grad_a_bruteforce(np.abs(g), np.abs(w))
+    assert np.allclose(S, S_bf, rtol=1e-13, atol=0)
+
+
+def test_grad_a_single_weight_probe():
+    """One nonzero weight at (n0, k0) moves column n0 of grad_out into column k0 of grad_A."""
+    M, N, K = 3, 5, 128
+    n0, k0 = 3, 70
+    b = np.full((N, K // 2), 0x77, dtype=np.uint8)         # all codes 7 -> 0.0
+    byte = b[n0, k0 // 2]
+    b[n0, k0 // 2] = (byte & 0xF0) | 15 if k0 % 2 == 0 else (byte & 0x0F) | (15 << 4)
+    s = np.full((N, K // 64), 0.75, dtype=np.float32)
+    g = synth.grad_out_normal(M, N, seed=5)
+    ref, _ = oracle.grad_a(g, s, b, M, N, K)
+    want = np.zeros((M, K))
+    want[:, k0] = g[:, n0].astype(np.float64) * 0.75
+    assert np.array_equal(ref, want)
+
+
+def test_grad_a_one_hot_rows_reproduce_dequant_rows():
+    M, N, K = 6, 9, 192
+    b = synth.random_code_bytes(N, K, seed=21)
+    s = synth.random_scales_uniform(N, K, seed=22)
+    g = np.zeros((M, N), dtype=np.float32)
+    picks = [0, 8, 3, 3, 5, 1]
+    for m, n in enumerate(picks):
+        g[m, n] = 1.0
+    ref, _ = oracle.grad_a(g, s, b, M, N, K)
+    w = oracle.dequant(s, b, N, K)
+    for m, n in enumerate(picks):
+        assert np.array_equal(ref[m], w[n].astype(np.float64))
+
+
+def test_grad_a_adjoint_identity():
+    """<grad_A, A> = <grad_out, A . W^T> with (A . W^T)[m][n] = sum_k A[m][k] W[n][k]."""
+    M, N, K = 7, 48, 256
+    b = synth.random_code_bytes(N, K, seed=31)
+    s = synth.random_scales_uniform(N, K, seed=32)
+    g = synth.grad_out_normal(M, N, seed=33)
+    A = synth.grad_out_normal(M, K, seed=34)
+    ref, _ = oracle.grad_a(g, s, b, M, N, K)
+    w = oracle.dequant(s, b, N, K).astype(np.float64)
+    fwd = np.einsum("mk,nk->mn", A.astype(np.float64), w)
+    lhs = np.sum(ref * A)
+    rhs = np.sum(g.astype(np.float64) * fwd)
+    assert abs(lhs - rhs) <= 1e-11 * (np.sum(np.abs(ref * A)) + 1.0)
+
+
+def test_grad_a_special_cases():
+    M, N, K = 5, 40, 128
+    g = synth.grad_out_normal(M, N, seed=41)
+    # all codes 7 -> level 0 -> grad_A identically zero
+    b7 = np.full((N, K // 2), 0x77, dtype=np.uint8)
+    s = synth.random_scales_uniform(N, K, seed=42)
+    ref, _ = oracle.grad_a(g, s, b7, M, N, K)
+    assert np.all(ref == 0.0)
+    # unit scales, all codes 15 -> every column is the row sum of grad_out
+    bF = np.full((N, K // 2), 0xFF, dtype=np.uint8)
+    ones = np.ones((N, K // 64), dtype=np.float32)
+    ref, _ = oracle.grad_a(g, ones, bF, M, N, K)
+    rs = np.sum(g.astype(np.float64), axis=1)
+    assert np.allclose(ref, np.repeat(rs[:, None], K, axis=1), rtol=1e-14, atol=1e-14)
+    # unit scales, random codes -> sum over levels of level * (grad_out @ one-hot(code == level))
+    b = synth.random_code_bytes(N, K, seed=43)
+    ref, _ = oracle.grad_a(g, ones, b, M, N, K)
+    lo = (b & 0x0F).astype(np.int64)
+    hi = (b >> 4).astype(np.int64)
+    alt = np.zeros((M, K))
+    for v in range(16):
+        onehot = np.zeros((N, K))
+        onehot[:, 0::2] = lo == v
+        onehot[:, 1::2] = hi == v
+        alt += float(oracle.NF4_LEVELS[v]) * (g.astype(np.float64) @ onehot)
+    assert np.allclose(ref, alt, rtol=1e-12, atol=1e-12)
+
+
+def test_fp16_operand_reference_rounds_to_nearest_even():
+    """The diagnostic reference converts with RNE (ties to even), not toward zero."""
+    one = np.float32(1.0)
+    tie_down = np.float32(1.0 + 2.0 ** -11)        # halfway between 1 and 1+2^-10 -> 1 (even)
+    tie_up = np.float32(1.0 + 3 * 2.0 ** -11)      # halfway between 1+2^-10 and 1+2^-9 -> 1+2^-9
+    above = np.float32(1.0 + 2.0 ** -11 + 2.0 ** -20)
+    g = np.array([[1.0]], dtype=np.float32)
+    for val, want in [(tie_down, 1.0), (tie_up, 1.0 + 2.0 ** -9), (above, 1.0 + 2.0 ** -10), (one, 1.0)]:
+        # build a 1x64 weight row with scale=val and code 15 at k=0
+        b = np.full((1, 32), 0x77, dtype=np.uint8)
+        b[0, 0] = 0x7F
+        s = np.array([[val]], dtype=np.float32)
+        ref16, _ = oracle.grad_a_fp16_operands(g, s, b, 1, 1, 64)
+        assert ref16[0, 0] == want
+
+
+# ---------------------------------------------------------------------- pack
+
+def _pack_bruteforce(w_block):
+    """Exact rational argmin over the 16 levels, ties to the lower code."""
+    absmax = max(abs(Fraction(float(x))) for x in w_block)
+    if absmax == 0:
+        return 0.0, [7] * len(w_block)
+    levels = [Fraction(float(q)) for q in oracle.NF4_LEVELS]
+    codes = []
+    for x in w_block:
+        r = Fraction(float(x)) / absmax
+        dists = [abs(r - q) for q in levels]
+        best = min(dists)
+        codes.append(dists.index(best))          # first index = lower code on ties
+    return float(absmax), codes
+
+
+def test_pack_matches_exact_rational_argmin():
+    N, K = 3, 128
+    w = synth.weights_normal(N, K, seed=51)
+    scales, b = oracle.pack(w, N, K)
+    codes = oracle.unpack_codes(b, N, K)
+    for n in range(N):
+        for kb in range(K // 64):
+            blk = w[n, kb * 64:(kb + 1) * 64]
+            a, c = _pack_bruteforce(blk)
+            assert scales[n, kb] == a
+            assert list(codes[n, kb * 64:(kb + 1) * 64]) == c
+
+
+def test_pack_exact_ties_go_to_lower_code():
+    # absmax 1.0; q6/2 and q8/2 are exact midpoints against level 0.0 and are fp32-representable
+    q = oracle.NF4_LEVELS
+    row = np.zeros(64, dtype=np.float32)
+    row[0] = 1.0
+    row[1] = q[6] / 2          # tie between codes 6 and 7 -> 6
+    row[2] = q[8] / 2          # tie between codes 7 and 8 -> 7
+    row[3] = -1.0              # tie-free endpoint -> 0
+    row[4] = np.nextafter(np.float32(q[8] / 2), np.float32(1))  # just above -> 8
+    _, b = oracle.pack(row[None, :], 1, 64)
+    c = oracle.unpack_codes(b, 1, 64)[0]
+    assert list(c[:5]) == [15, 6, 7, 0, 8]
+    for i, x in enumerate(row[:5]):
+        assert _pack_bruteforce(row)[1][i] == c[i]
+
+
+def test_pack_special_blocks_and_round_trip():
+    N, K = 4, 256
+    w = synth.weights_normal(N, K, seed=61)
+    w[1, 64:128] = 0.0                            # an all-zero block
+    w[2, 0:64] = -0.0
+    scales, b = oracle.pack(w, N, K)
+    codes = oracle.unpack_codes(b, N, K)
+    assert scales[1, 1] == 0.0 and np.all(codes[1, 64:128] == 7)
+    assert scales[2, 0] == 0.0 and np.all(codes[2, 0:64] == 7)
+    back = oracle.dequant(scales, b, N, K)
+    for n in range(N):
+        for kb in range(K // 64):
+            blk = w[n, kb * 64:(kb + 1) * 64]
+            a = scales[n, kb]
+            # the max half-gap between neighbouring levels is below 0.152
+            assert np.all(np.abs(back[n, kb * 64:(kb + 1) * 64].astype(np.float64) - blk)
+                          <= 0.152 * float(a) * (1 + 1e-6))
+            if a > 0:
+                i = int(np.argmax(np.abs(blk)))
+                assert abs(float(back[n, kb * 64 + i])) == float(a)   # the absmax element is exact
+                assert codes[n, kb * 64 + i] in (0, 15)
