@@ -1,0 +1,173 @@
+"""Python binding over the NF4 input-gradient C ABI (``include/nf4bwd.h``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libnf4bwd.so``.  PyTorch supplies device memory and the current
+stream.  Importing this module loads the in-tree library and fails loudly if
+it is missing; there is no fallback of any kind.
+
+    grad_a(grad_out, scales, codes)  -> fp32 [M, K]
+    dequant(scales, codes, N, K)     -> fp32 [N, K]
+    pack(w)                          -> (scales fp32 [N, K/64], codes uint8 [N, K/2])
+
+Tensors must be contiguous, on the current CUDA (HIP) device, 16-byte
+aligned, with the dtypes and shapes the C ABI states.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libnf4bwd.so")
+
+NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_HIP = 0, 1, 2, 3, 4
+
+EXPORTED_SYMBOLS = ("nf4_grad_a", "nf4_dequant", "nf4_pack", "nf4_status_string", "nf4_grad_a_plan",
+                    "nf4_grad_a_forced")
+
+
+class Nf4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python dequant_backward_gemm_amd/build.py` "
+            "(hipcc, gfx950). There is no CPU fallback.")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.nf4_grad_a.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.nf4_grad_a.restype = ctypes.c_int
+    lib.nf4_dequant.argtypes = [vp, vp, vp, i64, i64, vp]
+    lib.nf4_dequant.restype = ctypes.c_int
+    lib.nf4_pack.argtypes = [vp, vp, vp, i64, i64, vp]
+    lib.nf4_pack.restype = ctypes.c_int
+    lib.nf4_status_string.argtypes = [ctypes.c_int]
+    lib.nf4_status_string.restype = ctypes.c_char_p
+    lib.nf4_grad_a_plan.argtypes = [i64, i64, i64, ctypes.POINTER(ctypes.c_int)]
+    lib.nf4_grad_a_plan.restype = ctypes.c_int
+    ci = ctypes.c_int
+    lib.nf4_grad_a_forced.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, ci, vp]
+    lib.nf4_grad_a_forced.restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def status_string(status: int) -> str:
+    return _lib.nf4_status_string(int(status)).decode()
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream) -> int | None:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(status: int, what: str) -> None:
+    if status != NF4_OK:
+        raise Nf4Error(status, what)
+
+
+def _require(t, dtype, shape, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def grad_a_raw(grad_out_ptr, scales_ptr, codes_ptr, grad_a_ptr, M, N, K, stream_handle) -> int:
+    """Direct C-ABI call with raw pointers; returns the nf4_status."""
+    return _lib.nf4_grad_a(grad_out_ptr, scales_ptr, codes_ptr, grad_a_ptr, M, N, K, stream_handle)
+
+
+def dequant_raw(scales_ptr, codes_ptr, w_ptr, N, K, stream_handle) -> int:
+    return _lib.nf4_dequant(scales_ptr, codes_ptr, w_ptr, N, K, stream_handle)
+
+
+def pack_raw(w_ptr, scales_ptr, codes_ptr, N, K, stream_handle) -> int:
+    return _lib.nf4_pack(w_ptr, scales_ptr, codes_ptr, N, K, stream_handle)
+
+
+def grad_a(grad_out, scales, codes, out=None, stream=None):
+    """grad_A[M, K] = grad_out[M, N] . dequant(codes, scales)[N, K] (fp32)."""
+    import torch
+    M, N = grad_out.shape
+    K = codes.shape[1] * 2
+    _require(grad_out, torch.float32, (M, N), "grad_out")
+    _require(scales, torch.float32, (N, K // 64), "scales")
+    _require(codes, torch.uint8, (N, K // 2), "codes")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float32, device=grad_out.device)
+    _require(out, torch.float32, (M, K), "out")
+    _check(grad_a_raw(_ptr(grad_out), _ptr(scales), _ptr(codes), _ptr(out), M, N, K, _stream_handle(stream)),
+           "nf4_grad_a")
+    return out
+
+
+def grad_a_forced(grad_out, scales, codes, kernel: str, rb: int = 2, splits: int = 1, out=None, stream=None):
+    """grad_a with a forced launch plan (kernel "tile" or "skinny"); for tests and tuning."""
+    import torch
+    M, N = grad_out.shape
+    K = codes.shape[1] * 2
+    _require(grad_out, torch.float32, (M, N), "grad_out")
+    _require(scales, torch.float32, (N, K // 64), "scales")
+    _require(codes, torch.uint8, (N, K // 2), "codes")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float32, device=grad_out.device)
+    _require(out, torch.float32, (M, K), "out")
+    kid = {"tile": 0, "skinny": 1}[kernel]
+    _check(_lib.nf4_grad_a_forced(_ptr(grad_out), _ptr(scales), _ptr(codes), _ptr(out), M, N, K, kid, rb, splits,
+                                  _stream_handle(stream)), "nf4_grad_a_forced")
+    return out
+
+
+def dequant(scales, codes, out=None, stream=None):
+    """w[N, K] = fl32(scales[n, k/64] * NF4[code(n, k)])."""
+    import torch
+    N = codes.shape[0]
+    K = codes.shape[1] * 2
+    _require(scales, torch.float32, (N, K // 64), "scales")
+    _require(codes, torch.uint8, (N, K // 2), "codes")
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.float32, device=codes.device)
+    _require(out, torch.float32, (N, K), "out")
+    _check(dequant_raw(_ptr(scales), _ptr(codes), _ptr(out), N, K, _stream_handle(stream)), "nf4_dequant")
+    return out
+
+
+def pack(w, scales=None, codes=None, stream=None):
+    """NF4-quantise fp32 weights w[N, K] -> (scales [N, K/64], codes [N, K/2])."""
+    import torch
+    N, K = w.shape
+    _require(w, torch.float32, (N, K), "w")
+    if scales is None:
+        scales = torch.empty((N, K // 64), dtype=torch.float32, device=w.device)
+    if codes is None:
+        codes = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    _require(scales, torch.float32, (N, K // 64), "scales")
+    _require(codes, torch.uint8, (N, K // 2), "codes")
+    _check(pack_raw(_ptr(w), _ptr(scales), _ptr(codes), N, K, _stream_handle(stream)), "nf4_pack")
+    return scales, codes
+
+
+def grad_a_plan(M: int, N: int, K: int) -> dict:
+    """Launch plan nf4_grad_a uses for a shape (host-only, no device work)."""
+    out = (ctypes.c_int * 5)()
+    _check(_lib.nf4_grad_a_plan(M, N, K, out), "nf4_grad_a_plan")
+    kernel = {0: "tile", 1: "skinny", 2: "zero_fill"}[out[0]]
+    return {"kernel": kernel, "rb": out[1], "splits": out[2], "n_chunk": out[3], "grid": out[4]}

@@ -1,0 +1,90 @@
+// C ABI of the NF4 input-gradient library: argument validation, then the
+// launchers.  Declarations and the contract are in include/nf4bwd.h.
+#include <stdint.h>
+
+#include "nf4_launch.h"
+#include "nf4bwd.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = 0x7fffffffLL;        // every dimension fits an int
+constexpr int64_t kMaxElems = (1LL << 40);       // any one array: at most 2^40 elements
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dims_ok(int64_t a, int64_t b) {
+  if (a < 0 || b < 0 || a > kMaxDim || b > kMaxDim) return false;
+  return a == 0 || b <= kMaxElems / a;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int nf4_grad_a(const float* grad_out, const float* scales, const uint8_t* codes, float* grad_a, int64_t M,
+               int64_t N, int64_t K, hipStream_t stream) {
+  if (!dims_ok(M, N) || !dims_ok(N, K) || !dims_ok(M, K) || (K % 64) != 0) return NF4_ERR_SHAPE;
+  if (M == 0 || K == 0) return NF4_OK;
+  if (grad_a == nullptr) return NF4_ERR_NULL;
+  if (N > 0 && (grad_out == nullptr || scales == nullptr || codes == nullptr)) return NF4_ERR_NULL;
+  if (!aligned16(grad_a) || (N > 0 && (!aligned16(grad_out) || !aligned16(scales) || !aligned16(codes))))
+    return NF4_ERR_ALIGN;
+  return from_hip(nf4::launch_grad_a(grad_out, scales, codes, grad_a, M, N, K, stream));
+}
+
+int nf4_dequant(const float* scales, const uint8_t* codes, float* w_out, int64_t N, int64_t K, hipStream_t stream) {
+  if (!dims_ok(N, K) || (K % 64) != 0) return NF4_ERR_SHAPE;
+  if (N == 0 || K == 0) return NF4_OK;
+  if (scales == nullptr || codes == nullptr || w_out == nullptr) return NF4_ERR_NULL;
+  if (!aligned16(scales) || !aligned16(codes) || !aligned16(w_out)) return NF4_ERR_ALIGN;
+  return from_hip(nf4::launch_dequant(scales, codes, w_out, N, K, stream));
+}
+
+int nf4_pack(const float* w, float* scales, uint8_t* codes, int64_t N, int64_t K, hipStream_t stream) {
+  if (!dims_ok(N, K) || (K % 64) != 0) return NF4_ERR_SHAPE;
+  if (N * (K / 64) * 8 / 256 > kMaxDim) return NF4_ERR_SHAPE;  // one thread per 8 weights
+  if (N == 0 || K == 0) return NF4_OK;
+  if (w == nullptr || scales == nullptr || codes == nullptr) return NF4_ERR_NULL;
+  if (!aligned16(w) || !aligned16(scales) || !aligned16(codes)) return NF4_ERR_ALIGN;
+  return from_hip(nf4::launch_pack(w, scales, codes, N, K, stream));
+}
+
+int nf4_grad_a_forced(const float* grad_out, const float* scales, const uint8_t* codes, float* grad_a,
+                      int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, hipStream_t stream) {
+  if (!dims_ok(M, N) || !dims_ok(N, K) || !dims_ok(M, K) || (K % 64) != 0) return NF4_ERR_SHAPE;
+  if (M == 0 || K == 0) return NF4_OK;
+  if (grad_a == nullptr) return NF4_ERR_NULL;
+  if (N > 0 && (grad_out == nullptr || scales == nullptr || codes == nullptr)) return NF4_ERR_NULL;
+  if (!aligned16(grad_a) || (N > 0 && (!aligned16(grad_out) || !aligned16(scales) || !aligned16(codes))))
+    return NF4_ERR_ALIGN;
+  nf4::GradAPlan p{};
+  if (!nf4::make_plan(M, N, K, kernel, rb, splits, &p)) return NF4_ERR_SHAPE;
+  return from_hip(nf4::launch_grad_a_plan(p, grad_out, scales, codes, grad_a, M, N, K, stream));
+}
+
+int nf4_grad_a_plan(int64_t M, int64_t N, int64_t K, int* out5) {
+  if (out5 == nullptr) return NF4_ERR_NULL;
+  if (!dims_ok(M, N) || !dims_ok(N, K) || !dims_ok(M, K) || (K % 64) != 0) return NF4_ERR_SHAPE;
+  const nf4::GradAPlan p = nf4::plan_grad_a(M, N, K);
+  out5[0] = p.kernel;
+  out5[1] = p.rb;
+  out5[2] = p.splits;
+  out5[3] = p.n_chunk;
+  out5[4] = p.grid;
+  return NF4_OK;
+}
+
+const char* nf4_status_string(int status) {
+  switch (status) {
+    case NF4_OK: return "ok";
+    case NF4_ERR_NULL: return "null pointer for a non-empty array";
+    case NF4_ERR_SHAPE: return "bad shape (negative size, K not a multiple of 64, or size too large)";
+    case NF4_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case NF4_ERR_HIP: return "HIP launch or stream-ordered allocation failed";
+    default: return "unknown nf4 status";
+  }
+}
+
+}  // extern "C"

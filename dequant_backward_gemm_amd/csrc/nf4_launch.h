@@ -1,0 +1,40 @@
+// Host-side launchers for the NF4 kernels.  Arguments are validated by the
+// C-ABI layer (nf4_abi.hip) before any of these is called: shapes are
+// non-negative, K % 64 == 0, every size fits the kernels' index types and
+// every pointer is 16-byte aligned.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nf4 {
+
+hipError_t launch_dequant(const float* scales, const uint8_t* codes, float* out, int64_t N, int64_t K,
+                          hipStream_t stream);
+
+hipError_t launch_pack(const float* w, float* scales, uint8_t* codes, int64_t N, int64_t K,
+                       hipStream_t stream);
+
+// grad_a[M][K] = grad_out[M][N] . dequant(codes, scales)[N][K]; M, K > 0, N >= 0.
+hipError_t launch_grad_a(const float* grad_out, const float* scales, const uint8_t* codes, float* grad_a,
+                         int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// Launch plan chosen for a shape (exposed for tests and the benchmark).
+struct GradAPlan {
+  int kernel;    // 0 = tile (BM = 128 * rb), 1 = skinny (M <= 16), 2 = zero-fill (N == 0)
+  int rb;        // 32-row blocks per wave (tile kernel)
+  int splits;    // number of N-chunks (1 = no workspace, no reduce launch)
+  int n_chunk;   // rows of N per chunk
+  int grid;      // workgroups of the main kernel
+};
+GradAPlan plan_grad_a(int64_t M, int64_t N, int64_t K);
+
+// Complete a forced plan (kernel, rb, splits) for a shape; returns false if
+// the combination is not valid for it.
+bool make_plan(int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, GradAPlan* out);
+
+// Launch a given plan.
+hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const float* scales, const uint8_t* codes,
+                              float* grad_a, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+}  // namespace nf4

@@ -1,0 +1,127 @@
+/*
+ * nf4bwd.h -- C ABI of the NF4-dequant-fused input-gradient GEMM for one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (aprender-gpu 0.32.0, src/kernels/backward/nf4_tensor_core.rs,
+ * doc comment of Nf4TensorCoreGemmBackwardAKernel):
+ *
+ *     grad_A[M x K] = grad_out[M x N] . dequant(B_nf4[K x N])^T
+ *
+ * the input gradient of a frozen 4-bit (NF4) linear layer.  K is the layer's
+ * in-features (the output dimension here), N its out-features (the reduction
+ * dimension), M the token count.
+ *
+ * Packed-weight format (same page, Phase 2, "NF4 addressing"): the stored
+ * array is W = B^T, N x K.  For every out-feature n its K codes are
+ * contiguous, two per byte, the even k in the low nibble:
+ *
+ *     codes  : uint8_t [N][K/2]      code(n,k) = (codes[n][k/2] >> 4*(k%2)) & 0xF
+ *     scales : float   [N][K/64]     one fp32 scale per (n, 64-wide block of k)
+ *
+ * so w[n][k] = fl32(scales[n][k/64] * NF4[code(n,k)]), one fp32 multiply
+ * (Phase 2, "NF4 LUT lookup + dequant").  NF4 is the 16-level NormalFloat-4
+ * codebook of QLoRA (Dettmers et al., 2023): level 7 is 0.0, level 15 is 1.0,
+ * level 0 is -1.0.  K must be a multiple of 64 (the page's block size).
+ *
+ * Shared rules for every entry point below:
+ *   - All array pointers are DEVICE pointers on the current HIP device; all
+ *     arrays are dense row-major with the shapes stated.  The caller owns every
+ *     buffer; the library never frees caller memory.
+ *   - Calls are asynchronous on `stream` (0 = the default stream).  They
+ *     return once the work is enqueued; the caller synchronises.
+ *   - Outputs must not alias inputs.
+ *   - Every pointer must be 16-byte aligned (128-bit loads and stores).
+ *   - Return value is an nf4_status; on any error other than NF4_ERR_HIP
+ *     nothing has been enqueued.  NF4_ERR_HIP reports a failed launch or a
+ *     failed stream-ordered allocation (hipGetLastError); the stream's later
+ *     work is then undefined.
+ *   - No state is kept across calls apart from a per-device property cache.
+ *     Concurrent calls on different streams are safe.
+ */
+#ifndef NF4BWD_H
+#define NF4BWD_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nf4_status {
+  NF4_OK = 0,
+  NF4_ERR_NULL = 1,   /* a required pointer is NULL while its array is non-empty */
+  NF4_ERR_SHAPE = 2,  /* negative size, K % 64 != 0, or a size over 2^31-1 */
+  NF4_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned */
+  NF4_ERR_HIP = 4     /* a HIP launch or stream-ordered allocation failed */
+} nf4_status;
+
+/*
+ * nf4_grad_a -- the fused input gradient (the page's four phases: grad_out
+ * fp32 -> fp16 operand, NF4 decode -> fp16 operand, fp16 products accumulated
+ * in fp32 over N, fp32 store).
+ *
+ *   grad_out : const float   [M][N]
+ *   scales   : const float   [N][K/64]
+ *   codes    : const uint8_t [N][K/2]
+ *   grad_a   : float         [M][K], OVERWRITTEN (no accumulate), as the
+ *              page's Phase 4 store does.
+ *
+ *   grad_a[m][k] = sum_n fp16(grad_out[m][n]) * fp16(w[n][k]), accumulated in
+ *   fp32, with fp16() round-to-nearest-even and w the fp32 dequantised weight.
+ *   Any M >= 0 and N >= 0 are accepted (tails are masked); N == 0 writes
+ *   zeros; M == 0 or K == 0 enqueues nothing.  Results are bitwise
+ *   deterministic for a given (M, N, K): no atomics, fixed summation order.
+ *   Large N may use a stream-ordered device workspace (hipMallocAsync on
+ *   `stream`, released on the same stream).
+ */
+int nf4_grad_a(const float* grad_out, const float* scales, const uint8_t* codes,
+               float* grad_a, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * nf4_dequant -- w_out[n][k] = fl32(scales[n][k/64] * NF4[code(n,k)]), fp32
+ * [N][K] (= W = B^T).  Bit-exact: one IEEE fp32 multiply per element.
+ */
+int nf4_dequant(const float* scales, const uint8_t* codes, float* w_out,
+                int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * nf4_pack -- quantise fp32 weights w[N][K] (= B^T, the nn.Linear layout) to
+ * NF4.  Per (n, 64-block): scales[n][kb] = max |w| over the block, stored as
+ * is; code = the level nearest to w/absmax, ties to the lower code, decided
+ * exactly as #{i : w > absmax * mid_i} in fp64 with mid_i the midpoint of
+ * levels i and i+1.  An all-zero block gets scale 0 and code 7.  Non-finite
+ * weights are outside the contract.
+ */
+int nf4_pack(const float* w, float* scales, uint8_t* codes,
+             int64_t N, int64_t K, hipStream_t stream);
+
+/* Human-readable text for an nf4_status value (static storage). */
+const char* nf4_status_string(int status);
+
+/*
+ * nf4_grad_a_plan -- host-only introspection of the launch plan nf4_grad_a
+ * uses for a shape (no device work).  out5 receives, in order: kernel
+ * (0 = tiled, 1 = skinny M <= 16, 2 = zero fill for N == 0), 32-row blocks
+ * per wave of the tiled kernel, number of N-chunks (1 = no workspace), rows
+ * per N-chunk, workgroups of the main launch.  Returns NF4_ERR_SHAPE /
+ * NF4_ERR_NULL like nf4_grad_a.
+ */
+int nf4_grad_a_plan(int64_t M, int64_t N, int64_t K, int* out5);
+
+/*
+ * nf4_grad_a_forced -- nf4_grad_a with the launch plan forced, for tests and
+ * tuning: kernel 0 = tiled with `rb` (1 or 2) 32-row blocks per wave, kernel
+ * 1 = skinny (requires M <= 16); `splits` = requested number of N-chunks
+ * (rounded so that every chunk but the last is a whole number of stages).
+ * Same contract and results-to-bound as nf4_grad_a; NF4_ERR_SHAPE if the
+ * forced plan does not fit the shape.
+ */
+int nf4_grad_a_forced(const float* grad_out, const float* scales, const uint8_t* codes, float* grad_a,
+                      int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NF4BWD_H */

@@ -1,0 +1,332 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded inputs.
+
+Bars:
+* nf4_dequant and nf4_pack: bit-exact.
+* nf4_grad_a: |gpu - ref| <= 2e-3 * S + 1e-6 element by element, with ref the
+  fp64 definition and S = sum_n |g * w|.  A tighter diagnostic compares with
+  the fp16-operand reference (sum_n fp16(g) * fp16(w) in fp64): the only
+  difference left there is fp32 accumulation, bounded by
+  (N/8 + 64) * 2^-24 * S16, which fp16 rounding in the wrong direction
+  (e.g. toward zero) would break at the small sizes used.
+Every input is seeded and synthetic; no expected value comes from the GPU.
+"""
+
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_within_bound(gpu, ref, S, what=""):
+    err = np.abs(gpu.astype(np.float64) - ref)
+    lim = 2e-3 * S + 1e-6
+    bad = err > lim
+    if bad.any():
+        i = np.unravel_index(np.argmax(err / lim), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} elements out of bound; worst at {i}: "
+                             f"gpu={gpu[i]!r} ref={ref[i]!r} S={S[i]!r}")
+    assert np.all(np.isfinite(gpu))
+
+
+def assert_fp16_diag(gpu, g, s, b, M, N, K, rows=None, what=""):
+    ref16, S16 = oracle.grad_a_fp16_operands(g, s, b, M, N, K, rows=rows)
+    tol = (N / 8 + 64) * 2.0 ** -24 * S16 + 1e-30
+    err = np.abs(gpu.astype(np.float64) - ref16)
+    bad = err > tol
+    if bad.any():
+        i = np.unravel_index(np.argmax(err / np.maximum(tol, 1e-300)), err.shape)
+        raise AssertionError(f"{what}: fp16-operand diagnostic failed at {i}: gpu={gpu[i]!r} "
+                             f"ref16={ref16[i]!r} tol={tol[i]!r}")
+
+
+@functools.lru_cache(maxsize=8)
+def packed_weights(N, K, seed):
+    """Oracle-quantised N(0, 0.02) weights (CPU): the inputs both sides use."""
+    w = synth.weights_normal(N, K, seed)
+    s, b = oracle.pack(w, N, K)
+    return s, b
+
+
+def random_inputs(M, N, K, seed):
+    b = synth.random_code_bytes(N, K, seed)
+    s = synth.random_scales_uniform(N, K, seed + 1)
+    g = synth.grad_out_normal(M, N, seed + 2)
+    return g, s, b
+
+
+def check_grad_a(nb, g, s, b, M, N, K, kernel=None, rb=2, splits=1, what="", diag=True):
+    gd, sd, bd = dev(g), dev(s), dev(b)
+    if kernel is None:
+        out = nb.grad_a(gd, sd, bd)
+    else:
+        out = nb.grad_a_forced(gd, sd, bd, kernel, rb=rb, splits=splits)
+    gpu = host(out)
+    ref, S = oracle.grad_a(g, s, b, M, N, K)
+    assert_within_bound(gpu, ref, S, what)
+    if diag:
+        assert_fp16_diag(gpu, g, s, b, M, N, K, what=what)
+    return gpu
+
+
+# ------------------------------------------------------------------ dequant
+
+@pytest.mark.parametrize("N,K", [(1, 64), (3, 128), (17, 320), (256, 256), (1536, 1536), (18944, 3584)])
+def test_dequant_bit_exact(lib, N, K):
+    b = synth.random_code_bytes(N, K, seed=N + K)
+    s = synth.random_scales_uniform(N, K, seed=N + K + 1)
+    w = host(lib.dequant(dev(s), dev(b)))
+    assert np.array_equal(w.view(np.uint32), oracle.dequant(s, b, N, K).view(np.uint32))
+
+
+def test_dequant_bit_exact_wide_scale_range(lib):
+    """Scales from 1e-40 (fp32 subnormal) to 1e30: products round exactly like the oracle, subnormals kept."""
+    N, K = 64, 512
+    rng = np.random.default_rng(7)
+    s = (10.0 ** rng.uniform(-40, 30, size=(N, K // 64))).astype(np.float32)
+    s *= np.where(rng.random(s.shape) < 0.5, -1, 1).astype(np.float32)
+    b = synth.random_code_bytes(N, K, seed=8)
+    w = host(lib.dequant(dev(s), dev(b)))
+    assert np.array_equal(w.view(np.uint32), oracle.dequant(s, b, N, K).view(np.uint32))
+
+
+# --------------------------------------------------------------------- pack
+
+@pytest.mark.parametrize("N,K", [(1, 64), (5, 192), (64, 1024), (1536, 1536), (3584, 3584)])
+def test_pack_bit_exact(lib, N, K):
+    w = synth.weights_normal(N, K, seed=N * 7 + K)
+    if N >= 5:
+        w[0, :64] = 0.0
+        w[1, :64] = -0.0
+        w[2, :64] = 0.0
+        w[2, 5] = 3.5
+        q = oracle.NF4_LEVELS
+        w[3, :64] = 0.0
+        w[3, 0] = 1.0
+        w[3, 1] = q[6] / 2          # exact tie -> lower code
+        w[3, 2] = q[8] / 2
+        w[4, 64 % K:64 % K + 64] = np.float32(2.0 ** -130)   # subnormal block
+    s, b = lib.pack(dev(w))
+    s_ref, b_ref = oracle.pack(w, N, K)
+    assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(host(b), b_ref)
+
+
+# ------------------------------------------------------------------- grad_A
+
+SMALL = [
+    # (M, N, K)
+    (1, 1, 64), (2, 17, 64), (8, 64, 128), (15, 100, 192), (16, 128, 256), (17, 64, 64),
+    (33, 200, 320), (100, 64, 512), (130, 257, 256), (257, 128, 192), (64, 1, 128),
+]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_grad_a_small_default_plan(lib, M, N, K):
+    g, s, b = random_inputs(M, N, K, seed=M * 1000 + N + K)
+    check_grad_a(lib, g, s, b, M, N, K, what=f"default {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("kernel,rb,splits", [("tile", 1, 1), ("tile", 2, 1), ("tile", 1, 3), ("tile", 2, 2),
+                                              ("skinny", 0, 1), ("skinny", 0, 3)])
+@pytest.mark.parametrize("M,N,K", [(1, 300, 320), (5, 200, 192), (16, 1000, 512), (3, 129, 64), (12, 64, 1088)])
+def test_grad_a_every_variant_small(lib, kernel, rb, splits, M, N, K):
+    g, s, b = random_inputs(M, N, K, seed=M + N * 3 + K * 5 + splits)
+    check_grad_a(lib, g, s, b, M, N, K, kernel=kernel, rb=max(rb, 1), splits=splits,
+                 what=f"{kernel} rb{rb} s{splits} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("kernel,rb,splits", [("tile", 1, 1), ("tile", 2, 1), ("tile", 2, 4), ("tile", 1, 2)])
+@pytest.mark.parametrize("M,N,K", [(200, 384, 768), (300, 100, 320), (513, 640, 256)])
+def test_grad_a_tile_variants_ragged(lib, kernel, rb, splits, M, N, K):
+    g, s, b = random_inputs(M, N, K, seed=M + N + K + rb * 11 + splits)
+    check_grad_a(lib, g, s, b, M, N, K, kernel=kernel, rb=rb, splits=splits,
+                 what=f"{kernel} rb{rb} s{splits} {M}x{N}x{K}")
+
+
+PAGE_SHAPES = [(128, 1536, 1536), (64, 256, 128), (16, 64, 64), (512, 1536, 1536), (512, 256, 1536),
+               (512, 4608, 1536), (512, 1536, 4608)]
+
+
+@pytest.mark.parametrize("M,N,K", PAGE_SHAPES)
+def test_grad_a_page_test_shapes(lib, M, N, K):
+    """The (m, n, k) triples of the subject page's own tests, packed N(0, 0.02) weights."""
+    s, b = packed_weights(N, K, seed=N + K)
+    g = synth.grad_out_normal(M, N, seed=M + 5, std=1e-2)
+    check_grad_a(lib, g, s, b, M, N, K, what=f"page {M}x{N}x{K}")
+
+
+def test_grad_a_tiny_config(lib):
+    g, s, b = synth.inputs.tiny_inputs(seed=0)
+    check_grad_a(lib, g, s, b, 64, 256, 256, what="tiny")
+
+
+def test_grad_a_attention_projection_config(lib):
+    M, N, K = 2048, 1536, 1536
+    s, b = packed_weights(N, K, seed=0)
+    g = synth.grad_out_normal(M, N, seed=0 + 100, std=1e-2)
+    check_grad_a(lib, g, s, b, M, N, K, what="attn_proj")
+
+
+@pytest.mark.parametrize("which,seed", [(0, 0), (1, 1)])
+def test_grad_a_mlp_pair_config(lib, which, seed):
+    shp = synth.CONFIGS["mlp_pair"][which]
+    M, N, K = shp.M, shp.N, shp.K
+    s, b = packed_weights(N, K, seed=seed)
+    g = synth.grad_out_normal(M, N, seed=seed + 100, std=1e-2)
+    check_grad_a(lib, g, s, b, M, N, K, what=shp.name, diag=False)
+
+
+@pytest.mark.parametrize("shp", synth.SKINNY_SHAPES, ids=lambda s: s.name)
+def test_grad_a_skinny_config(lib, shp):
+    M, N, K = shp.M, shp.N, shp.K
+    seed = 0 if K == 3584 else 1
+    s, b = packed_weights(N, K, seed=seed)
+    g = synth.grad_out_normal(M, N, seed=10 + M, std=1.0)
+    check_grad_a(lib, g, s, b, M, N, K, what=shp.name)
+
+
+@pytest.mark.parametrize("proj", ["q", "k", "gate", "down"])
+def test_grad_a_full_step_shapes_sampled_rows(lib, proj):
+    """Full-step projections at M = 8192 with the production plan; 16 rows checked."""
+    N, K = {p: (n, k) for (p, n, k) in synth.FULL_STEP_PROJECTIONS}[proj]
+    M = 8192
+    s, b = packed_weights(N, K, seed=100 + ["q", "k", "v", "o", "gate", "up", "down"].index(proj))
+    g = synth.grad_out_normal(M, N, seed=200, std=1e-2)
+    out = lib.grad_a(dev(g), dev(s), dev(b))
+    gpu = host(out)
+    assert np.all(np.isfinite(gpu))
+    rng = np.random.default_rng(300)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, size=14)]))
+    ref, S = oracle.grad_a(g, s, b, M, N, K, rows=rows)
+    assert_within_bound(gpu[rows], ref, S, f"full_step {proj}")
+
+
+# ------------------------------------------------- metamorphic / exact checks
+
+def test_grad_a_deterministic(lib):
+    M, N, K = 300, 4000, 512
+    g, s, b = random_inputs(M, N, K, seed=9)
+    gd, sd, bd = dev(g), dev(s), dev(b)
+    for kernel, rb, splits in [("tile", 2, 3), ("tile", 1, 1)]:
+        r1 = host(lib.grad_a_forced(gd, sd, bd, kernel, rb=rb, splits=splits))
+        r2 = host(lib.grad_a_forced(gd, sd, bd, kernel, rb=rb, splits=splits))
+        assert np.array_equal(r1.view(np.uint32), r2.view(np.uint32))
+    g1 = g[:7]
+    r1 = host(lib.grad_a(dev(g1), sd, bd))
+    r2 = host(lib.grad_a(dev(g1), sd, bd))
+    assert np.array_equal(r1.view(np.uint32), r2.view(np.uint32))
+
+
+@pytest.mark.parametrize("M", [5, 200])
+def test_grad_a_power_of_two_scaling_is_exact(lib, M):
+    N, K = 640, 512
+    g, s, b = random_inputs(M, N, K, seed=17)
+    g = np.sign(g) * np.clip(np.abs(g), 2.0 ** -12, 1000.0)  # fp16 images stay normal
+    g = g.astype(np.float32)
+    base = host(lib.grad_a(dev(g), dev(s), dev(b)))
+    twice_g = host(lib.grad_a(dev(g * 2), dev(s), dev(b)))
+    half_s = host(lib.grad_a(dev(g), dev(s * np.float32(0.5)), dev(b)))
+    assert np.array_equal(twice_g, base * 2)
+    assert np.array_equal(half_s, base * 0.5)
+
+
+@pytest.mark.parametrize("M", [6, 40])
+def test_grad_a_one_hot_rows_give_fp16_dequant_rows(lib, M):
+    N, K = 96, 320
+    b = synth.random_code_bytes(N, K, seed=21)
+    s = synth.random_scales_uniform(N, K, seed=22)
+    g = np.zeros((M, N), dtype=np.float32)
+    picks = np.random.default_rng(23).integers(0, N, size=M)
+    g[np.arange(M), picks] = 1.0
+    gpu = host(lib.grad_a(dev(g), dev(s), dev(b)))
+    w16 = oracle.dequant(s, b, N, K).astype(np.float16).astype(np.float32)
+    assert np.array_equal(gpu, w16[picks])
+
+
+def test_grad_a_operand_rounding_of_grad_out(lib):
+    """A single weight 1.0 at (n0, k0): column k0 of grad_A is fp16(grad_out[:, n0]) exactly."""
+    M, N, K = 70, 64, 256
+    n0, k0 = 37, 201
+    b = np.full((N, K // 2), 0x77, dtype=np.uint8)
+    b[n0, k0 // 2] = 0xF7 if k0 % 2 else 0x7F
+    s = np.ones((N, K // 64), dtype=np.float32)
+    g = synth.grad_out_normal(M, N, seed=29)
+    gpu = host(lib.grad_a(dev(g), dev(s), dev(b)))
+    want = np.zeros((M, K), dtype=np.float32)
+    want[:, k0] = g[:, n0].astype(np.float16).astype(np.float32)
+    assert np.array_equal(gpu, want)
+
+
+def test_grad_a_adjoint_identity(lib):
+    M, N, K = 48, 700, 384
+    g, s, b = random_inputs(M, N, K, seed=31)
+    A = synth.grad_out_normal(M, K, seed=34)
+    gpu = host(lib.grad_a(dev(g), dev(s), dev(b))).astype(np.float64)
+    w = oracle.dequant(s, b, N, K).astype(np.float64)
+    _, S = oracle.grad_a(g, s, b, M, N, K)
+    lhs = np.sum(gpu * A)
+    rhs = np.sum(g.astype(np.float64) * (A.astype(np.float64) @ w.T))
+    assert abs(lhs - rhs) <= np.sum(np.abs(A) * (2e-3 * S + 1e-6))
+
+
+def test_grad_a_on_side_stream(lib):
+    M, N, K = 64, 256, 256
+    g, s, b = random_inputs(M, N, K, seed=41)
+    st = torch.cuda.Stream()
+    gd, sd, bd = dev(g), dev(s), dev(b)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(st):
+        out = lib.grad_a(gd, sd, bd)
+    st.synchronize()
+    ref, S = oracle.grad_a(g, s, b, M, N, K)
+    assert_within_bound(out.cpu().numpy(), ref, S, "side stream")
+
+
+# --------------------------------------------------------------- edge cases
+
+def test_grad_a_empty_and_degenerate(lib):
+    K = 128
+    # N == 0: empty sum -> zeros (overwrites whatever was there)
+    out = torch.full((5, K), 7.0, device="cuda")
+    g = torch.empty((5, 0), device="cuda")
+    s = torch.empty((0, K // 64), device="cuda")
+    b = torch.empty((0, K // 2), dtype=torch.uint8, device="cuda")
+    lib.grad_a(g, s, b, out=out)
+    assert torch.count_nonzero(out).item() == 0
+    # M == 0: nothing happens
+    out0 = lib.grad_a(torch.empty((0, 64), device="cuda"), torch.ones((64, 2), device="cuda"),
+                      torch.zeros((64, 64), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert tuple(out0.shape) == (0, 128)
+
+
+def test_grad_a_rejects_bad_arguments_on_device(lib):
+    M, N, K = 8, 64, 128
+    g = torch.zeros((M, N + 1), device="cuda")
+    s = torch.ones((N, K // 64), device="cuda")
+    b = torch.zeros((N, K // 2), dtype=torch.uint8, device="cuda")
+    out = torch.zeros((M, K), device="cuda")
+    hs = torch.cuda.current_stream().cuda_stream
+    # misaligned grad_out (offset by one float)
+    st = lib.grad_a_raw(g.data_ptr() + 4, s.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K, hs)
+    assert st == lib.NF4_ERR_ALIGN
+    st = lib.grad_a_raw(g.data_ptr(), s.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K + 1, hs)
+    assert st == lib.NF4_ERR_SHAPE
+    with pytest.raises(lib.Nf4Error):
+        lib.grad_a_forced(torch.zeros((17, N), device="cuda"), s, b, "skinny")   # skinny needs M <= 16
