@@ -1,0 +1,277 @@
+"""Benchmark of the NF4-dequant-fused input-gradient GEMM on one MI355X.
+
+One "step" is the input-gradient work of one training step of a 7B-class
+decoder with NF4-frozen base weights: 28 layers x 7 projections (q, k, v, o,
+gate, up, down) at M = 8192 tokens, issued in backward order (layer 27 -> 0;
+down, up, gate, o, v, k, q), 196 calls of nf4_grad_a.  Inputs are synthetic
+and resident in HBM before timing: weights ~ N(0, 0.02) quantised on the
+device with nf4_pack, grad_out ~ N(0, 1e-2).
+
+Printed on stdout: ONE JSON line.  `value` is whole-step throughput in
+TFLOP/s (2*M*N*K summed over the 196 calls, divided by the measured step
+time).  `roofline` covers the dominant kernel (the tiled grad_A kernel at the
+gate/up/down shapes, 2*8192*18944*3584 flop per launch) with HIP events
+around every such launch inside the timed steps.  `cpu_baseline` is the fp64
+CPU oracle timed on a bounded sample.  `per_config` holds the four smaller
+workloads (tiny, attention projection, MLP pair, skinny sweep), timed with
+rotated input sets so they do not sit in the 256 MB Infinity Cache.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-configs]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_FP16_TFLOPS = 2500.0   # MI355X dense fp16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+LAYERS = 28
+PROJ = [("q", 3584, 3584), ("k", 512, 3584), ("v", 512, 3584), ("o", 3584, 3584),
+        ("gate", 18944, 3584), ("up", 18944, 3584), ("down", 3584, 18944)]
+BACKWARD_ORDER = ["down", "up", "gate", "o", "v", "k", "q"]
+M_STEP = 8192
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def alg_bytes(M, N, K):
+    return 4 * M * N + K * N // 2 + K * N // 16 + 4 * M * K
+
+
+def roofline_time(M, N, K):
+    return max(2.0 * M * N * K / (PEAK_FP16_TFLOPS * 1e12), alg_bytes(M, N, K) / (PEAK_HBM_GBS * 1e9))
+
+
+def build_full_step(torch, nb):
+    """Packed weights for all 196 projections, one grad_out and one grad_A per projection type."""
+    gen = torch.Generator(device="cuda")
+    weights = {}
+    for layer in range(LAYERS):
+        for pi, (p, N, K) in enumerate(PROJ):
+            gen.manual_seed(1000 * layer + pi)
+            w = torch.empty((N, K), device="cuda", dtype=torch.float32)
+            w.normal_(0.0, 0.02, generator=gen)
+            weights[(layer, p)] = nb.pack(w)
+            del w
+    gen.manual_seed(7)
+    gouts, outs = {}, {}
+    for (p, N, K) in PROJ:
+        g = torch.empty((M_STEP, N), device="cuda", dtype=torch.float32)
+        g.normal_(0.0, 1e-2, generator=gen)
+        gouts[p] = g
+        outs[p] = torch.empty((M_STEP, K), device="cuda", dtype=torch.float32)
+    torch.cuda.synchronize()
+    return weights, gouts, outs
+
+
+def run_step(nb, weights, gouts, outs, events=None):
+    for layer in range(LAYERS - 1, -1, -1):
+        for p in BACKWARD_ORDER:
+            s, c = weights[(layer, p)]
+            if events is not None and p in events:
+                e0, e1 = events[p].pop()
+                e0.record()
+                nb.grad_a(gouts[p], s, c, out=outs[p])
+                e1.record()
+                events[p + "_done"].append((e0, e1))
+            else:
+                nb.grad_a(gouts[p], s, c, out=outs[p])
+
+
+def time_config(torch, nb, M, N, K, seed, g_std, rotate_bytes=512 << 20, target_s=0.02, trials=5):
+    """Median per-call time of nf4_grad_a over rotated input sets (each set: codes, scales, grad_out)."""
+    per_set = alg_bytes(M, N, K)
+    nsets = max(2, -(-rotate_bytes // per_set))
+    nsets = min(nsets, 64)
+    gen = torch.Generator(device="cuda")
+    sets = []
+    for i in range(nsets):
+        gen.manual_seed(seed * 100 + i)
+        w = torch.empty((N, K), device="cuda").normal_(0.0, 0.02, generator=gen)
+        s, c = nb.pack(w)
+        del w
+        g = torch.empty((M, N), device="cuda").normal_(0.0, g_std, generator=gen)
+        o = torch.empty((M, K), device="cuda")
+        sets.append((g, s, c, o))
+    torch.cuda.synchronize()
+    for i in range(5):
+        g, s, c, o = sets[i % nsets]
+        nb.grad_a(g, s, c, out=o)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    nb.grad_a(*sets[0][:3], out=sets[0][3])
+    torch.cuda.synchronize()
+    one = max(time.perf_counter() - t0, 1e-6)
+    reps = int(min(max(target_s / one, 2 * nsets), 20000))
+    res = []
+    for _ in range(trials):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(reps):
+            g, s, c, o = sets[r % nsets]
+            nb.grad_a(g, s, c, out=o)
+        e1.record()
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) * 1e-3 / reps)
+    del sets
+    torch.cuda.empty_cache()
+    res.sort()
+    return res[len(res) // 2], res[0], res[-1], nsets
+
+
+def per_config_table(torch, nb):
+    import synth
+    out = {}
+    plan = [("tiny", synth.CONFIGS["tiny"], 1.0), ("attn_proj", synth.CONFIGS["attn_proj"], 1e-2),
+            ("mlp_pair", synth.CONFIGS["mlp_pair"], 1e-2), ("skinny", synth.SKINNY_SHAPES, 1.0)]
+    for cname, shapes, gstd in plan:
+        for i, shp in enumerate(shapes):
+            med, lo, hi, nsets = time_config(torch, nb, shp.M, shp.N, shp.K, seed=i, g_std=gstd)
+            fl = 2.0 * shp.M * shp.N * shp.K
+            by = alg_bytes(shp.M, shp.N, shp.K)
+            tf = fl / med / 1e12
+            gb = by / med / 1e9
+            bound = "mfma" if fl / (PEAK_FP16_TFLOPS * 1e12) >= by / (PEAK_HBM_GBS * 1e9) else "hbm"
+            out[shp.name] = {
+                "M": shp.M, "N": shp.N, "K": shp.K, "us": round(med * 1e6, 2),
+                "us_min": round(lo * 1e6, 2), "us_max": round(hi * 1e6, 2),
+                "tflops": round(tf, 2), "gbs": round(gb, 1), "bound": bound,
+                "frac_of_bound": round(tf / PEAK_FP16_TFLOPS if bound == "mfma" else gb / PEAK_HBM_GBS, 4),
+                "frac_of_roofline_time": round(roofline_time(shp.M, shp.N, shp.K) / med, 4),
+                "rotated_input_sets": nsets, "plan": nb.grad_a_plan(shp.M, shp.N, shp.K),
+            }
+            log(f"[bench] {shp.name}: {med * 1e6:.1f} us  {tf:.1f} TFLOP/s  {gb:.0f} GB/s")
+    return out
+
+
+def cpu_baseline():
+    """The fp64 oracle, as it stands, on a bounded sample of one full-step layer."""
+    import numpy as np
+    import oracle
+    import synth
+    rows = 256
+    flops = 0.0
+    t = 0.0
+    for pi, (p, N, K) in enumerate(PROJ):
+        b = synth.random_code_bytes(N, K, seed=pi)
+        s = synth.random_scales_uniform(N, K, seed=pi + 10)
+        g = synth.grad_out_normal(rows, N, seed=pi + 20, std=1e-2)
+        t0 = time.perf_counter()
+        oracle.grad_a(g, s, b, rows, N, K, with_bound=False)
+        t += time.perf_counter() - t0
+        flops += 2.0 * rows * N * K
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except Exception:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": min(cores, threads),
+            "kind": "oracle", "seconds": round(t, 2),
+            "sample": f"one layer's 7 projections of the full step (q,k,v,o,gate,up,down) at {rows} of the 8192 "
+                      f"token rows each: numpy fp64 dequant + matmul, {flops / 1e9:.1f} GFLOP"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-config table")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the NF4 input-gradient GEMM "
+              "needs no collective and is benchmarked on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dequant_backward_gemm_amd as nb
+
+    props = torch.cuda.get_device_properties(0)
+    log(f"[bench] device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+    t_setup = time.perf_counter()
+    weights, gouts, outs = build_full_step(torch, nb)
+    log(f"[bench] full-step inputs ready in {time.perf_counter() - t_setup:.1f} s")
+
+    step_flops = sum(2.0 * M_STEP * N * K for (_, N, K) in PROJ) * LAYERS
+    step_roof = sum(roofline_time(M_STEP, N, K) for (_, N, K) in PROJ) * LAYERS
+
+    for _ in range(args.warmup):
+        run_step(nb, weights, gouts, outs)
+    torch.cuda.synchronize()
+
+    dom = ("gate", "up", "down")
+    events = {}
+    for p in dom:
+        events[p] = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(LAYERS * args.steps)]
+        events[p + "_done"] = []
+
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        run_step(nb, weights, gouts, outs, events)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / args.steps
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    log(f"[bench] step {ms_per_step:.2f} ms ({value:.1f} TFLOP/s), wall {wall:.2f} s for {args.steps} steps")
+
+    durs = [a.elapsed_time(b) * 1e-3 for p in dom for (a, b) in events[p + "_done"]]
+    avg = sum(durs) / len(durs)
+    launch_flops = 2.0 * M_STEP * 18944 * 3584
+    achieved = launch_flops / avg / 1e12
+    plan = nb.grad_a_plan(M_STEP, 18944, 3584)
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": None,
+            "kernel": f"grad_a_tile_kernel<{plan['rb']}>", "launches": len(durs),
+            "avg_launch_us": round(avg * 1e6, 1), "flop_per_launch": launch_flops}
+
+    per_config = None if args.no_configs else per_config_table(torch, nb)
+    cpu = None if args.no_cpu else cpu_baseline()
+
+    rec = {
+        "metric": "NF4 grad_A GEMM TFLOP/s (2MNK/t) + % of MFMA or HBM roofline, per config",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": "full_step: 28 layers x 7 NF4 projections (q,o 3584x3584; k,v 3584->512; gate,up "
+                        "3584->18944; down 18944->3584), M=8192 tokens, NF4 block 64, fp32 grad_out/grad_A",
+            "calls_per_step": LAYERS * len(PROJ),
+            "step_gflop": round(step_flops / 1e9, 1),
+            "step_roofline_ms": round(step_roof * 1e3, 3),
+            "frac_of_roofline_time": round(step_roof * 1e3 / ms_per_step, 4),
+            "device": props.name,
+            "cus": props.multi_processor_count,
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_config": per_config,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -30,6 +30,8 @@ HIPCC_FLAGS = [
     # fp32 denormals kept (IEEE), no fast-math: the decode multiply and the
     # fp16 conversions must be the IEEE operations.
     "-fno-gpu-flush-denormals-to-zero",
+    # LDS buffers are viewed with several element types
+    "-fno-strict-aliasing",
     # no packed-fp32 VALU instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
