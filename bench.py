@@ -9,14 +9,18 @@ device with nf4_pack, grad_out ~ N(0, 1e-2).
 
 Printed on stdout: ONE JSON line.  `value` is whole-step throughput in
 TFLOP/s (2*M*N*K summed over the 196 calls, divided by the measured step
-time).  `roofline` covers the dominant kernel (the tiled grad_A kernel at the
-gate/up/down shapes, 2*8192*18944*3584 flop per launch) with HIP events
-around every such launch inside the timed steps.  `cpu_baseline` is the fp64
-CPU oracle timed on a bounded sample.  `per_config` holds the four smaller
-workloads (tiny, attention projection, MLP pair, skinny sweep), timed with
-rotated input sets so they do not sit in the 256 MB Infinity Cache.
+time).  `roofline` covers the dominant kernel -- the grad_A kernel with the
+most time in the step -- from HIP events recorded around every call inside
+the timed steps: achieved = its FLOPs / its summed launch durations.
+`traffic` is the HBM bytes per launch from the committed counter summary in
+profiles/, reported only when that summary was taken on the current kernel
+source.  `cpu_baseline` is the fp64 CPU oracle timed on a bounded sample.
+`per_config` holds the four smaller workloads (tiny, attention projection,
+MLP pair, skinny sweep), timed with rotated input sets so they do not sit in
+the 256 MB Infinity Cache.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-configs]
+       python bench.py --copy-calibration   (1 GiB device copy, for counter scaling)
 """
 
 from __future__ import annotations
@@ -72,17 +76,69 @@ def build_full_step(torch, nb):
 
 
 def run_step(nb, weights, gouts, outs, events=None):
+    """One step: 196 calls in backward order.  With `events`, record an event pair around each call."""
     for layer in range(LAYERS - 1, -1, -1):
         for p in BACKWARD_ORDER:
             s, c = weights[(layer, p)]
-            if events is not None and p in events:
-                e0, e1 = events[p].pop()
+            if events is not None:
+                e0, e1 = events["free"].pop()
                 e0.record()
                 nb.grad_a(gouts[p], s, c, out=outs[p])
                 e1.record()
-                events[p + "_done"].append((e0, e1))
+                events["done"].append((p, e0, e1))
             else:
                 nb.grad_a(gouts[p], s, c, out=outs[p])
+
+
+def kernel_name_for(plan):
+    if plan["kernel"] == "skinny":
+        return "grad_a_skinny_kernel"
+    if plan["kernel"] == "zero_fill":
+        return "fill_zero_kernel"
+    return "grad_a_tile_kernel<%d>" % plan["rb"]
+
+
+def source_digest():
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in ("nf4_grad_a.hip", "nf4_device.h"):
+        with open(os.path.join(here, "dequant_backward_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", "grad_a_full_step_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_digest") != source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    n = 256 << 20  # floats: 1 GiB
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "copies": 3}), flush=True)
 
 
 def time_config(torch, nb, M, N, K, seed, g_std, rotate_bytes=512 << 20, target_s=0.02, trials=5):
@@ -186,6 +242,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config table")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for scaling HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the NF4 input-gradient GEMM "
@@ -193,6 +251,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     import dequant_backward_gemm_amd as nb
 
     props = torch.cuda.get_device_properties(0)
@@ -208,13 +269,9 @@ def main():
         run_step(nb, weights, gouts, outs)
     torch.cuda.synchronize()
 
-    dom = ("gate", "up", "down")
-    events = {}
-    for p in dom:
-        events[p] = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                     for _ in range(LAYERS * args.steps)]
-        events[p + "_done"] = []
-
+    calls = LAYERS * len(PROJ)
+    events = {"free": [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(calls * args.steps)], "done": []}
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -230,15 +287,28 @@ def main():
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     log(f"[bench] step {ms_per_step:.2f} ms ({value:.1f} TFLOP/s), wall {wall:.2f} s for {args.steps} steps")
 
-    durs = [a.elapsed_time(b) * 1e-3 for p in dom for (a, b) in events[p + "_done"]]
-    avg = sum(durs) / len(durs)
-    launch_flops = 2.0 * M_STEP * 18944 * 3584
-    achieved = launch_flops / avg / 1e12
-    plan = nb.grad_a_plan(M_STEP, 18944, 3584)
+    # Per-launch durations grouped by the kernel each call's plan launches; the dominant kernel is
+    # the one with the most total time.
+    shapes = {p: (N, K) for (p, N, K) in PROJ}
+    by_kernel = {}
+    for p, a, b in events["done"]:
+        N, K = shapes[p]
+        name = kernel_name_for(nb.grad_a_plan(M_STEP, N, K))
+        d = by_kernel.setdefault(name, [0.0, 0.0, 0])
+        d[0] += a.elapsed_time(b) * 1e-3
+        d[1] += 2.0 * M_STEP * N * K
+        d[2] += 1
+    dom = max(by_kernel, key=lambda k: by_kernel[k][0])
+    dsec, dflop, dn = by_kernel[dom]
+    achieved = dflop / dsec / 1e12
+    traffic = recorded_traffic()
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": None,
-            "kernel": f"grad_a_tile_kernel<{plan['rb']}>", "launches": len(durs),
-            "avg_launch_us": round(avg * 1e6, 1), "flop_per_launch": launch_flops}
+            "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": traffic,
+            "kernel": dom, "launches": dn, "avg_launch_us": round(dsec / dn * 1e6, 1),
+            "flop_per_launch": round(dflop / dn), "alg_bytes_per_launch":
+                round(sum(alg_bytes(M_STEP, N, K) for (_, N, K) in PROJ) / len(PROJ)),
+            "share_of_step_time": round(dsec / (ms_total * 1e-3), 4),
+            "kernel_source_digest": source_digest()}
 
     per_config = None if args.no_configs else per_config_table(torch, nb)
     cpu = None if args.no_cpu else cpu_baseline()

@@ -384,7 +384,9 @@ __global__ __launch_bounds__(256, 1) void grad_a_tile_fast_kernel(
   auto stage = [&](int st, int cur, const u32x4 (&afc)[RB][4], u32x4 (&afn)[RB][4]) {
     const uint32_t rbase = frag_lane + (uint32_t)(cur * 32768);
     const uint32_t wbase = frag_lane + (uint32_t)(((cur ^ 1) * 4 + wave) * 8 * 1024);
-    u32x4 ring[4];
+    // 8 registers for 4 slots of read-ahead: a reload never targets a register
+    // that an MFMA still in flight is reading
+    u32x4 ring[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) ring[i] = lds_load_u32x4(smem, rbase + (uint32_t)(i * 1024));
     uint32_t xd[8];
@@ -404,9 +406,10 @@ __global__ __launch_bounds__(256, 1) void grad_a_tile_fast_kernel(
         xd[k] = read_code(k);
         sd[k] = read_scale(k);
       }
-      acc[rb][i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(afc[rb][i >> 3]), as_half8(ring[i & 3]),
+      acc[rb][i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(afc[rb][i >> 3]), as_half8(ring[i & 7]),
                                                               acc[rb][i & 7], 0, 0, 0);
-      if constexpr (rb == RB - 1 && i + 4 < 32) ring[i & 3] = lds_load_u32x4(smem, rbase + (uint32_t)((i + 4) * 1024));
+      if constexpr (rb == RB - 1 && i + 4 < 32)
+        ring[(i + 4) & 7] = lds_load_u32x4(smem, rbase + (uint32_t)((i + 4) * 1024));
       if constexpr (k >= D0 && (k - D0) / P < 8 && (k - D0) % P < 4) {
         constexpr int t = (k - D0) / P, m = (k - D0) % P;
         lk[t & 1][2 * m] = lookup_x(xd[2 * m], t);
