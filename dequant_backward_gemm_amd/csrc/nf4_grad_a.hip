@@ -38,23 +38,11 @@
 // then one fp32 add per chunk), which keeps the rounding error far below the
 // 2e-3 * sum|g*w| acceptance bound at the largest N used.
 #include <algorithm>
-#include <type_traits>
-#include <utility>
 
-#include "nf4_device.h"
+#include "nf4_kernel_util.h"
 #include "nf4_launch.h"
 
 namespace nf4 {
-
-// Consecutive workgroup ids are dispatched round-robin over the 8 XCDs.
-// Map them so that the ids one XCD receives are consecutive in logical order.
-__device__ __forceinline__ int xcd_remap(int bid, int nblk) {
-  const int q = nblk >> 3, r = nblk & 7;
-  const int xcd = bid & 7, slot = bid >> 3;
-  return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
-}
-
-__device__ __forceinline__ half8 as_half8(u32x4 v) { return __builtin_bit_cast(half8, v); }
 
 // ---------------------------------------------------------------------------
 // Tile kernel (M > 16)
@@ -228,42 +216,6 @@ __global__ __launch_bounds__(256, (RB == 1 ? 2 : 1)) void grad_a_tile_kernel(
 //  * the decode of stage i+1 is spread between the MFMAs of stage i.
 constexpr int kLutBytes = 64;
 constexpr int kFragBytes = 2 * 4 * 8 * 64 * 16;
-
-// LDS accessors.  One LDS array is viewed with several element types (levels
-// as fp32, code words, packed fp16 fragments), so every access goes through a
-// may_alias type: without it, type-based alias analysis would let the
-// compiler reorder a read of one type above a write of another.
-typedef float f32_alias __attribute__((may_alias));
-typedef uint32_t u32_alias __attribute__((may_alias));
-typedef u32x4 u32x4_alias __attribute__((may_alias));
-
-__device__ __forceinline__ float lds_load_f32(const uint32_t* smem, uint32_t byte_addr) {
-  return *reinterpret_cast<const f32_alias*>(reinterpret_cast<const char*>(smem) + byte_addr);
-}
-__device__ __forceinline__ uint32_t lds_load_u32(const uint32_t* smem, uint32_t byte_addr) {
-  return *reinterpret_cast<const u32_alias*>(reinterpret_cast<const char*>(smem) + byte_addr);
-}
-__device__ __forceinline__ void lds_store_u32(uint32_t* smem, uint32_t byte_addr, uint32_t v) {
-  *reinterpret_cast<u32_alias*>(reinterpret_cast<char*>(smem) + byte_addr) = v;
-}
-__device__ __forceinline__ u32x4 lds_load_u32x4(const uint32_t* smem, uint32_t byte_addr) {
-  return *reinterpret_cast<const u32x4_alias*>(reinterpret_cast<const char*>(smem) + byte_addr);
-}
-__device__ __forceinline__ void lds_store_u32x4(uint32_t* smem, uint32_t byte_addr, u32x4 v) {
-  *reinterpret_cast<u32x4_alias*>(reinterpret_cast<char*>(smem) + byte_addr) = v;
-}
-
-// Calls f(std::integral_constant<int, K>{}) for K = 0, 1, ... in order, fully
-// expanded at compile time (each call sees K as a constant expression).
-template <class F, int... Ks>
-__device__ __forceinline__ void for_each_index(std::integer_sequence<int, Ks...>, F&& f) {
-  (f(std::integral_constant<int, Ks>{}), ...);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  // raw buffer (stride 0): offsets are byte offsets, reads past `bytes` return 0
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
 
 // Fast path for full stages (N % 64 == 0): 4 waves, each owning 64 rows x
 // 256 columns of grad_A (two 32-row MFMA blocks x 8 tiles, 256 fp32
@@ -701,38 +653,48 @@ GradAPlan plan_grad_a(int64_t M, int64_t N, int64_t K) {
     p.grid = (int)(tiles_k * splits);
     return p;
   }
-  // Tile kernel: pick BM (128 or 256) and the N split by a simple cost model:
-  // wave-quantised MFMA time plus the partial-sum traffic of a split.
+  // Tile kernels: pick the kernel, its tile and the N split by a simple cost
+  // model: wave-quantised MFMA time at a measured efficiency plus the
+  // partial-sum traffic of a split.
   const double cu_rate = 4096.0 * 2.4e9;  // fp16 MFMA flop/s per CU
   double best = 1e30;
-  for (int rb = 2; rb >= 1; --rb) {
-    const int64_t BM = 128 * rb;
-    // measured on MI355X: 128-row tiles (two workgroups per CU) reach ~24% of
-    // the fp16 MFMA rate, 256-row tiles (one per CU) ~19%
-    const int per_cu = (rb == 1) ? 2 : 1;
-    const double eff = (rb == 1) ? 0.24 : 0.19;
-    const int64_t tiles = cdiv(M, BM) * tiles_k;
-    const int64_t max_split = cdiv(N, 64);
+  // Splitting N pays only when the tiles alone leave most CUs idle: measured
+  // with the wide kernel, 48 tiles ran 9% faster split in two and 96 tiles 33%
+  // slower (partials, the reduce launch and cache pressure).  Problems under a
+  // GFLOP are launch-bound and never split.
+  const bool tiny = 2.0 * (double)M * (double)N * (double)K < 1e9;
+  auto consider = [&](int kernel, int param, int64_t BM, int64_t BK, int per_cu, double eff) {
+    const int64_t tiles = cdiv(M, BM) * cdiv(K, BK);
+    const int64_t max_split = (tiny || tiles >= 64) ? 1 : cdiv(N, 64);
     for (int64_t s = 1; s <= std::min<int64_t>(max_split, 16); ++s) {
       const int64_t chunk = cdiv(cdiv(N, s), 64) * 64;
       const int64_t se = cdiv(N, chunk);
       if (se != s) continue;
       const int64_t units = tiles * se;
       const int64_t rounds = cdiv(units, (int64_t)kCUs * per_cu);
-      const double t_unit = (double)BM * 256.0 * (double)chunk * 2.0 / (cu_rate * eff / per_cu);
-      double t = (double)rounds * t_unit;
+      const double t_unit = (double)BM * (double)BK * (double)chunk * 2.0 / (cu_rate * eff / per_cu);
+      double t = (double)rounds * t_unit + 3e-6;
       // split partials: written once and read once by the reduce kernel (measured ~2.5 TB/s
       // effective), plus the extra launch
       if (se > 1) t += 2.0 * (double)se * (double)M * (double)K * 4.0 / 2.5e12 + 8e-6;
       if (t < best * 0.999) {
         best = t;
-        p.kernel = 0;
-        p.rb = rb;
+        p.kernel = kernel;
+        p.rb = param;
         p.splits = (int)se;
         p.n_chunk = (int)chunk;
         p.grid = (int)units;
       }
     }
+  };
+  // measured on MI355X (fraction of the fp16 MFMA rate at M = 8192): tile
+  // kernel with 128-row tiles (two workgroups per CU) ~0.24, 256-row tiles
+  // ~0.19; wide kernel 512 x 128 tiles ~0.28, 256 x 256 tiles ~0.11
+  consider(0, 2, 256, 256, 1, 0.19);
+  consider(0, 1, 128, 256, 2, 0.24);
+  if (wide_kernel_supported(M, N, K)) {
+    consider(3, 1, wide_tile_rows(1), wide_tile_cols(1), 1, 0.28);
+    consider(3, 2, wide_tile_rows(2), wide_tile_cols(2), 1, 0.11);
   }
   return p;
 }
@@ -761,6 +723,14 @@ bool make_plan(int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, 
     p.n_chunk = (int)chunk;
     p.splits = (int)cdiv(N, chunk);
     p.grid = (int)(cdiv(M, 128 * rb) * tiles_k * p.splits);
+  } else if (kernel == 3) {
+    if ((rb != 1 && rb != 2) || !wide_kernel_supported(M, N, K)) return false;
+    const int64_t chunk = cdiv(cdiv(N, splits), 64) * 64;
+    p.kernel = 3;
+    p.rb = rb;
+    p.n_chunk = (int)chunk;
+    p.splits = (int)cdiv(N, chunk);
+    p.grid = (int)(cdiv(M, wide_tile_rows(rb)) * cdiv(K, wide_tile_cols(rb)) * p.splits);
   } else {
     return false;
   }
@@ -793,6 +763,14 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
   if (p.kernel == 1) {
     hipLaunchKernelGGL(grad_a_skinny_kernel, dim3(p.grid), dim3(256), 0, stream, grad_out, scales, c32, dst, (int)M,
                        (int)N, (int)K, p.n_chunk, tiles_k);
+  } else if (p.kernel == 3) {
+    const hipError_t e = launch_grad_a_wide(p.rb, p.grid, grad_out, scales, c32, dst, (int)M, (int)N, (int)K,
+                                            p.n_chunk, (int)cdiv(M, wide_tile_rows(p.rb)),
+                                            (int)cdiv(K, wide_tile_cols(p.rb)), stream);
+    if (e != hipSuccess) {
+      if (ws) (void)hipFreeAsync(ws, stream);
+      return e;
+    }
   } else {
     const int tiles_m = (int)cdiv(M, 128 * p.rb);
     // fast path: every stage of every chunk is full and every array has 32-bit byte offsets

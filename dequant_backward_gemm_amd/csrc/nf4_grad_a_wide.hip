@@ -1,0 +1,400 @@
+// Wide tile kernel for grad_A = grad_out . dequant(W) at large M, N % 64 == 0.
+//
+// Same arithmetic as the other grad_A kernels (grad_out rounded fp32 -> fp16,
+// weights fp16(fl32(scale * level)), fp16 MFMA products accumulated in fp32
+// over N), organised for two waves per SIMD:
+//
+// * A workgroup is 8 waves (512 threads).  Each wave owns 64 rows x 128
+//   columns of grad_A: four 16-row blocks x eight 16x16x32 MFMA tiles, 128
+//   fp32 accumulators per lane, so two waves fit one SIMD and one wave's MFMAs
+//   run while the other waits on memory or decodes.  The waves are arranged
+//   WR x WC over the tile: BM = 64 * WR rows by BK = 128 * WC columns.
+// * grad_out reaches the MFMA A operand through coalesced loads and an
+//   in-register transpose.  The A layout wants one grad_out row per lane
+//   (lanes i, i+16, i+32, i+48 share row i), and loads in that pattern touch a
+//   different cache line in every lane, which the vector memory pipe serves at
+//   a third of its rate.  So each group of four lanes loads 64 contiguous
+//   bytes of one row, the values are rounded to fp16, and four lane-bit
+//   exchanges (DPP selects for lane bits 0 and 1, permlane swaps for 4 and 5)
+//   move the two low lane bits (the 16-byte chunk within the 64) up to lane
+//   bits 4..5 and bring row bits down, ending in the A layout.
+// * The reduction is walked in stages of 64 rows of N (two k-steps of 32).
+//   Per stage every lane of the workgroup does a slice of three jobs:
+//     - tables: for each (row n, 64-column scale block) of a stage, the 16
+//       weights a code can stand for, fp16(fl32(scale * level)), are computed
+//       once and written to LDS (32 bytes per table).  Decoding a weight is then
+//       one table read -- no multiply and no conversion per weight;
+//     - decode: a lane takes one dword of codes (8 columns) from each of two
+//       adjacent rows n, n+1 and, per column, reads both rows' fp16 weights
+//       from their tables and packs them into one dword, which is exactly one
+//       register of an MFMA B operand (consecutive reduction indices at one
+//       column), and stores it into the fragment buffer in LDS;
+//     - MFMA: a wave multiplies its grad_out rows (converted on load) by the
+//       B fragments of the current stage.
+//   Tables are built two stages ahead and fragments one stage ahead, each in a
+//   double buffer, with one barrier per stage.
+// * Columns are permuted inside a tile so that every lane owns 8 consecutive
+//   outputs per row: column c of MFMA tile t (t = 0..7) in column group wc is
+//   k = k0 + 128*wc + 8*c + t.  A decoding lane's 8 columns are one code dword,
+//   and each goes to a different tile at the same lane column.  Inside a
+//   stage, k-step s, lane quarter q and element e is reduction row
+//   n = n0 + 32*s + 16*(e/4) + 4*q + e%4 for both operands (what the transpose
+//   of grad_out produces; consecutive pairs of n stay in one register).
+// * Table slots are permuted so that the 16 tables a wave instruction reads
+//   (random codes) fall in distinct 8-bank groups per half-wave; fragment
+//   writes and reads are lane-linear, so no access has bank conflicts.
+//
+// Every global load is in bounds by clamping (rows of grad_out past M, code
+// columns past K, stages past the end of a chunk); such values only reach
+// outputs that are never stored or buffers that are never read.
+#include "nf4_kernel_util.h"
+#include "nf4_launch.h"
+
+namespace nf4 {
+
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+template <int WC>
+struct WideCfg {
+  static constexpr int WR = 8 / WC;
+  static constexpr int BM = 64 * WR;
+  static constexpr int BK = 128 * WC;
+  static constexpr int KB = BK / 64;                      // scale blocks per tile row
+  static constexpr int kTabStage = 64 * KB * 32;          // 64 rows x KB tables x 16 fp16
+  static constexpr int kFragStage = 2 * WC * 8 * 64 * 16; // [k-step][wc][tile][lane] x 16 B
+  static constexpr int kTabBase = 0;
+  static constexpr int kFragBase = 2 * kTabStage;
+  static constexpr int kLds = kFragBase + 2 * kFragStage;
+};
+
+// Table slot (row n * KB + block) -> position in units of 32 bytes.  Slots are
+// permuted inside aligned groups of four so that the tables of the four row
+// pairs a half-wave reads at once sit in four different 8-bank groups.
+template <int KB>
+__device__ __forceinline__ uint32_t table_pos(uint32_t slot) {
+  return (slot & ~3u) | ((slot + slot / (2 * KB)) & 3u);
+}
+
+template <int WC>
+__global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
+    const float* __restrict__ G, const float* __restrict__ S, const uint32_t* __restrict__ C32,
+    float* __restrict__ out, int M, int N, int K, int n_chunk, int tiles_m, int tiles_k) {
+  using Cfg = WideCfg<WC>;
+  constexpr int WR = Cfg::WR, BM = Cfg::BM, BK = Cfg::BK, KB = Cfg::KB;
+  constexpr uint32_t kTabStage = Cfg::kTabStage, kFragStage = Cfg::kFragStage;
+  __shared__ __attribute__((aligned(16))) uint32_t smem[Cfg::kLds / 4];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int ci = lane & 15, q = lane >> 4;  // MFMA lane: row / column index, quarter
+  const int wr = wave % WR, wc = wave / WR;
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int kt = logical % tiles_k;
+  const int rest = logical / tiles_k;
+  const int mt = rest % tiles_m;
+  const int split = rest / tiles_m;
+  const int m0 = mt * BM, k0 = kt * BK;
+  const int nb = split * n_chunk;
+  const int ne = min(N, nb + n_chunk);
+  const int nst = (ne - nb) >> 6;
+
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(C32, (uint32_t)((size_t)N * (size_t)K / 2));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, (uint32_t)((size_t)N * (size_t)(K / 64) * 4));
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(G, (uint32_t)((size_t)M * (size_t)N * 4));
+  const uint32_t crow = (uint32_t)K / 2;   // bytes per code row
+  const uint32_t srow = (uint32_t)K / 16;  // bytes per scale row
+  auto stage_row = [&](int st) { return (uint32_t)(nb + 64 * min(st, nst - 1)); };
+
+  // ---- MFMA role: rows 64*wr + 16*rb + ci of the tile, reduction quarter q ----
+  // grad_out load v (0..7) of a k-step: row 16*(lane/16) + 4*((lane/4)%4) + v/2
+  // of the wave's 64, 16-byte chunk 4*(v%2) + lane%4 of the k-step's 128 bytes.
+  uint32_t voff_g[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = min(m0 + 64 * wr + 16 * (lane >> 4) + 4 * ((lane >> 2) & 3) + u, M - 1);
+    voff_g[u] = (uint32_t)row * (uint32_t)N * 4u + 16u * (uint32_t)(lane & 3);
+  }
+  const uint32_t rbase = Cfg::kFragBase + (uint32_t)wc * 8192u + 16u * lane;
+
+  // ---- decode role: rows (nr0, nr0 + 1) of a stage, code dword 16*v + dl ----
+  // wave w covers stage rows 8w .. 8w+7 (k-step w/4, quarter w%4), lane pair p
+  const int p = lane & 3, dl = lane >> 2;
+  const int nr0 = 8 * wave + 2 * p;
+  // Code columns past K (last tile) read the next row, or zero past the end of
+  // the array; they only reach columns that are never stored.
+  const uint32_t cvoff = (uint32_t)nr0 * crow + (uint32_t)(k0 / 2 + 4 * dl);
+  uint32_t tb[WC][2];
+#pragma unroll
+  for (int v = 0; v < WC; ++v) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const uint32_t slot = (uint32_t)((nr0 + r) * KB + 2 * v + (dl >> 3));
+      tb[v][r] = Cfg::kTabBase + table_pos<KB>(slot) * 32u;
+    }
+  }
+  // fragment dword written for column c of code dword 16*v + dl: k-step wave/4,
+  // group v, tile c; the rows' place n % 32 = 8*(wave%4) + 2p in the k-step is
+  // lane quarter (n % 16) / 4, register 2*(n / 16) + (n % 4) / 2
+  const uint32_t wb = Cfg::kFragBase + (uint32_t)(wave >> 2) * WC * 8192u +
+                      (uint32_t)(dl + 16 * (2 * (wave & 1) + (p >> 1))) * 16u +
+                      4u * (uint32_t)(2 * ((wave >> 1) & 1) + (p & 1));
+
+  // ---- table role: slot (tid / 4) + 128 * u, levels 4 * (tid % 4) .. + 3 ----
+  // (slot + 128 is row + 128 / KB of the same block, and its table sits 4 KiB
+  // further; scale blocks past K read like code columns past K.)
+  const int qq = tid & 3;
+  const int sl0 = tid >> 2;
+  const uint32_t svoff = (uint32_t)(sl0 / KB) * srow + 4u * (uint32_t)(k0 / 64 + sl0 % KB);
+  const uint32_t twaddr = Cfg::kTabBase + table_pos<KB>((uint32_t)sl0) * 32u + 8u * qq;
+  float lv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lv[i] = kLevels[4 * qq + i];
+
+  floatx4_t acc[4][8];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[rb][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto load_codes = [&](int st, uint32_t (&x)[WC][2]) {
+    const uint32_t r0 = stage_row(st);
+#pragma unroll
+    for (int v = 0; v < WC; ++v) {
+      x[v][0] = __builtin_amdgcn_raw_buffer_load_b32(rc, cvoff + 64u * v, r0 * crow, 0);
+      x[v][1] = __builtin_amdgcn_raw_buffer_load_b32(rc, cvoff + 64u * v, (r0 + 1) * crow, 0);
+    }
+  };
+  auto load_scales = [&](int st, float (&sc)[WC]) {
+    const uint32_t r0 = stage_row(st);
+#pragma unroll
+    for (int u = 0; u < WC; ++u)
+      sc[u] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rs, svoff, (r0 + (uint32_t)(u * 128 / KB)) * srow, 0));
+  };
+  auto build_tables = [&](const float (&sc)[WC], uint32_t toff) {
+#pragma unroll
+    for (int u = 0; u < WC; ++u) {
+      u32x2 w;
+      w[0] = pack_half2_rne(sc[u] * lv[0], sc[u] * lv[1]);
+      w[1] = pack_half2_rne(sc[u] * lv[2], sc[u] * lv[3]);
+      lds_store_u32x2(smem, twaddr + toff + 4096u * u, w);
+    }
+  };
+  // grad_out of k-step s of a stage, loaded coalesced (see voff_g)
+  auto load_a = [&](int st, int s, float (&a)[8][4]) {
+    const uint32_t soff = stage_row(st) * 4u;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const floatx4 x = __builtin_bit_cast(
+          floatx4, __builtin_amdgcn_raw_buffer_load_b128(rg, voff_g[v >> 1] + (uint32_t)(128 * s + 64 * (v & 1)), soff, 0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[v][e] = x[e];
+    }
+  };
+  // fp16 rounding, then the lane-bit exchanges that turn the load layout into
+  // the A layout.  Register index v = (v2 v1 v0) and lane = (l5 .. l0): loaded,
+  // l1 l0 = chunk bits C1 C0, v0 = C2, (l3 l2 v2 v1) = row bits R3..R0 and
+  // l5 l4 = R5 R4.  Exchanging l0 <-> v1, l1 <-> v2, l4 <-> v1, l5 <-> v2 gives
+  // lane = (C1 C0 R3 R2 R1 R0) = (q, i) and v = (R5 R4 C2) = (row block, half).
+  auto to_a_frags = [&](const float (&a)[8][4], u32x4 (&af)[4]) {
+    uint32_t r[8][2];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      r[v][0] = pack_half2_rne(a[v][0], a[v][1]);
+      r[v][1] = pack_half2_rne(a[v][2], a[v][3]);
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {  // l0 <-> v1: pairs (v, v + 2), v in {4g, 4g + 1}
+      uint32_t lo[4] = {r[4 * g][0], r[4 * g][1], r[4 * g + 1][0], r[4 * g + 1][1]};
+      uint32_t hi[4] = {r[4 * g + 2][0], r[4 * g + 2][1], r[4 * g + 3][0], r[4 * g + 3][1]};
+      xchg_lane_lo4<0>(lo, hi);
+      r[4 * g][0] = lo[0]; r[4 * g][1] = lo[1]; r[4 * g + 1][0] = lo[2]; r[4 * g + 1][1] = lo[3];
+      r[4 * g + 2][0] = hi[0]; r[4 * g + 2][1] = hi[1]; r[4 * g + 3][0] = hi[2]; r[4 * g + 3][1] = hi[3];
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {  // l1 <-> v2: pairs (v, v + 4), v in {2g, 2g + 1}
+      uint32_t lo[4] = {r[2 * g][0], r[2 * g][1], r[2 * g + 1][0], r[2 * g + 1][1]};
+      uint32_t hi[4] = {r[2 * g + 4][0], r[2 * g + 4][1], r[2 * g + 5][0], r[2 * g + 5][1]};
+      xchg_lane_lo4<1>(lo, hi);
+      r[2 * g][0] = lo[0]; r[2 * g][1] = lo[1]; r[2 * g + 1][0] = lo[2]; r[2 * g + 1][1] = lo[3];
+      r[2 * g + 4][0] = hi[0]; r[2 * g + 4][1] = hi[1]; r[2 * g + 5][0] = hi[2]; r[2 * g + 5][1] = hi[3];
+    }
+#pragma unroll
+    for (int v = 0; v < 8; ++v)  // l4 <-> v1
+      if ((v & 2) == 0) {
+        xchg_lane_hi<4>(r[v][0], r[v + 2][0]);
+        xchg_lane_hi<4>(r[v][1], r[v + 2][1]);
+      }
+#pragma unroll
+    for (int v = 0; v < 8; ++v)  // l5 <-> v2
+      if ((v & 4) == 0) {
+        xchg_lane_hi<5>(r[v][0], r[v + 4][0]);
+        xchg_lane_hi<5>(r[v][1], r[v + 4][1]);
+      }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      af[rb][0] = r[2 * rb][0];
+      af[rb][1] = r[2 * rb][1];
+      af[rb][2] = r[2 * rb + 1][0];
+      af[rb][3] = r[2 * rb + 1][1];
+    }
+  };
+
+  uint32_t y[WC][2], z[WC][2];  // code nibbles times two: low nibbles (even columns), high (odd)
+  auto prep = [&](const uint32_t (&x)[WC][2]) {
+#pragma unroll
+    for (int v = 0; v < WC; ++v)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        y[v][r] = (x[v][r] << 1) & 0x1E1E1E1Eu;
+        z[v][r] = (x[v][r] >> 3) & 0x1E1E1E1Eu;
+      }
+  };
+  // Decode of column c: the two table reads, then (after other work) the pack
+  // of both rows into one B-operand dword and its store.
+  auto lookup_col = [&](auto cc, uint32_t toff, uint32_t (&lk)[WC][2]) {
+    constexpr int c = decltype(cc)::value;
+#pragma unroll
+    for (int v = 0; v < WC; ++v) {
+      const uint32_t s0 = (c & 1) ? z[v][0] : y[v][0];
+      const uint32_t s1 = (c & 1) ? z[v][1] : y[v][1];
+      lk[v][0] = lds_load_u16(smem, add_byte<(c >> 1)>(tb[v][0], s0) + toff);
+      lk[v][1] = lds_load_u16(smem, add_byte<(c >> 1)>(tb[v][1], s1) + toff);
+    }
+  };
+  auto store_col = [&](auto cc, uint32_t foff, const uint32_t (&lk)[WC][2]) {
+    constexpr int c = decltype(cc)::value;
+#pragma unroll
+    for (int v = 0; v < WC; ++v)
+      lds_store_u32(smem, wb + foff + (uint32_t)(v * 8192 + c * 1024), lk[v][0] | (lk[v][1] << 16));
+  };
+
+  float ar[8][4];       // grad_out of the next k-step, as loaded
+  uint32_t xc[WC][2];   // codes of the stage decoded during the current one
+  float sc[WC];         // scales of the tables built during the current stage
+
+  // Prologue: tables of stages 0 and 1, stage 0 decoded into fragment buffer 0.
+  {
+    float s0[WC], s1[WC];
+    uint32_t x0[WC][2];
+    load_scales(0, s0);
+    load_scales(1, s1);
+    load_codes(0, x0);
+    load_codes(1, xc);
+    load_a(0, 0, ar);
+    load_scales(2, sc);
+    build_tables(s0, 0);
+    build_tables(s1, kTabStage);
+    __syncthreads();
+    prep(x0);
+    for_each_index(std::make_integer_sequence<int, 8>{}, [&](auto cc) {
+      uint32_t lk[WC][2];
+      lookup_col(cc, 0u, lk);
+      store_col(cc, 0u, lk);
+    });
+    __syncthreads();
+  }
+
+  // One stage: MFMAs on fragment buffer P, decode of stage st+1 into buffer
+  // P^1 with tables P^1, tables of stage st+2 into table buffer P.
+  auto stage = [&](int st, auto par) {
+    constexpr uint32_t P = decltype(par)::value;
+    constexpr uint32_t toff_dec = (P ^ 1u) * kTabStage, toff_build = P * kTabStage;
+    constexpr uint32_t frd = P * kFragStage, fwr = (P ^ 1u) * kFragStage;
+    uint32_t xn[WC][2];
+    float scn[WC];
+    prep(xc);
+    // k-step s: convert grad_out of s and issue the loads of the next k-step,
+    // then 8 ticks, one per MFMA tile t (4 MFMAs, one per row block).  B
+    // fragments are read two ticks ahead through a ring of three; the decode
+    // of columns 4s .. 4s+3 of the next stage (table reads, then two ticks
+    // later the pack and fragment store) and the per-stage extras are spread
+    // over the ticks.  Scheduling barriers between ticks keep every load where
+    // it is issued (the compiler would otherwise sink loads to their uses).
+    for_each_index(std::make_integer_sequence<int, 2>{}, [&](auto sc_) {
+      constexpr int s = decltype(sc_)::value;
+      constexpr int c0 = 4 * s;  // decode columns c0 .. c0 + 3 in this k-step
+      u32x4 af[4];
+      to_a_frags(ar, af);
+      __builtin_amdgcn_sched_barrier(0);  // transpose temporaries die before the next loads' registers
+      load_a(s == 0 ? st : st + 1, s ^ 1, ar);
+      auto read_b = [&](int t) { return lds_load_u32x4(smem, rbase + frd + (uint32_t)((s * WC * 8 + t) * 1024)); };
+      u32x4 bf[3];
+      bf[0] = read_b(0);
+      bf[1] = read_b(1);
+      uint32_t lk[2][WC][2];
+      __builtin_amdgcn_sched_barrier(0);
+      for_each_index(std::make_integer_sequence<int, 8>{}, [&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+          acc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(af[rb]), as_half8(bf[t % 3]), acc[rb][t], 0, 0, 0);
+        if constexpr (t + 2 < 8) bf[(t + 2) % 3] = read_b(t + 2);
+        if constexpr (t >= 2 && t < 6) store_col(std::integral_constant<int, c0 + t - 2>{}, fwr, lk[t & 1]);
+        if constexpr (t < 4) lookup_col(std::integral_constant<int, c0 + t>{}, toff_dec, lk[t & 1]);
+        if constexpr (t == 6 && s == 0) load_codes(st + 2, xn);
+        if constexpr (t == 6 && s == 1) load_scales(st + 3, scn);
+        if constexpr (t == 7 && s == 0) build_tables(sc, toff_build);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < WC; ++v) {
+      xc[v][0] = xn[v][0];
+      xc[v][1] = xn[v][1];
+      sc[v] = scn[v];
+    }
+  };
+
+  int st = 0;
+  for (; st + 1 < nst; st += 2) {
+    stage(st, std::integral_constant<uint32_t, 0>{});
+    stage(st + 1, std::integral_constant<uint32_t, 1>{});
+  }
+  if (st < nst) stage(st, std::integral_constant<uint32_t, 0>{});
+
+  // 16x16 accumulator layout: lane (ci, q), register r -> row 4*q + r, column ci.
+  float* __restrict__ dst = out + (size_t)split * (size_t)M * (size_t)K;
+  const int col = k0 + 128 * wc + 8 * ci;
+  if (col < K) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + 64 * wr + 16 * rb + 4 * q + r;
+        if (row < M) {
+          const floatx4 lo = {acc[rb][0][r], acc[rb][1][r], acc[rb][2][r], acc[rb][3][r]};
+          const floatx4 hi = {acc[rb][4][r], acc[rb][5][r], acc[rb][6][r], acc[rb][7][r]};
+          floatx4* o = reinterpret_cast<floatx4*>(dst + (size_t)row * (size_t)K + col);
+          o[0] = lo;
+          o[1] = hi;
+        }
+      }
+    }
+  }
+}
+
+bool wide_kernel_supported(int64_t M, int64_t N, int64_t K) {
+  return N > 0 && (N % 64) == 0 && (uint64_t)M * (uint64_t)N * 4 < (1ull << 31) &&
+         (uint64_t)N * (uint64_t)K / 2 < (1ull << 31);
+}
+
+int wide_tile_rows(int wc) { return wc == 2 ? WideCfg<2>::BM : WideCfg<1>::BM; }
+int wide_tile_cols(int wc) { return wc == 2 ? WideCfg<2>::BK : WideCfg<1>::BK; }
+
+hipError_t launch_grad_a_wide(int wc, int grid, const float* grad_out, const float* scales, const uint32_t* codes,
+                              float* dst, int M, int N, int K, int n_chunk, int tiles_m, int tiles_k,
+                              hipStream_t stream) {
+  if (wc == 2)
+    hipLaunchKernelGGL(grad_a_wide_kernel<2>, dim3(grid), dim3(512), 0, stream, grad_out, scales, codes, dst, M, N, K,
+                       n_chunk, tiles_m, tiles_k);
+  else
+    hipLaunchKernelGGL(grad_a_wide_kernel<1>, dim3(grid), dim3(512), 0, stream, grad_out, scales, codes, dst, M, N, K,
+                       n_chunk, tiles_m, tiles_k);
+  return hipGetLastError();
+}
+
+}  // namespace nf4

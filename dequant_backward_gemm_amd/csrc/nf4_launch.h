@@ -21,8 +21,9 @@ hipError_t launch_grad_a(const float* grad_out, const float* scales, const uint8
 
 // Launch plan chosen for a shape (exposed for tests and the benchmark).
 struct GradAPlan {
-  int kernel;    // 0 = tile (BM = 128 * rb), 1 = skinny (M <= 16), 2 = zero-fill (N == 0)
-  int rb;        // 32-row blocks per wave (tile kernel)
+  int kernel;    // 0 = tile (BM = 128 * rb), 1 = skinny (M <= 16), 2 = zero-fill (N == 0),
+                 // 3 = wide (8 waves, tile (512 / rb) x (128 * rb))
+  int rb;        // tile: 32-row blocks per wave; wide: 128-column groups
   int splits;    // number of N-chunks (1 = no workspace, no reduce launch)
   int n_chunk;   // rows of N per chunk
   int grid;      // workgroups of the main kernel
@@ -36,5 +37,14 @@ bool make_plan(int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, 
 // Launch a given plan.
 hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const float* scales, const uint8_t* codes,
                               float* grad_a, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// Wide tile kernel (nf4_grad_a_wide.hip): usable when N % 64 == 0 and the
+// operands have 32-bit byte offsets; tile shape for a column-group count.
+bool wide_kernel_supported(int64_t M, int64_t N, int64_t K);
+int wide_tile_rows(int wc);
+int wide_tile_cols(int wc);
+hipError_t launch_grad_a_wide(int wc, int grid, const float* grad_out, const float* scales, const uint32_t* codes,
+                              float* dst, int M, int N, int K, int n_chunk, int tiles_m, int tiles_k,
+                              hipStream_t stream);
 
 }  // namespace nf4

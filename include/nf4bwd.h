@@ -102,17 +102,20 @@ const char* nf4_status_string(int status);
 /*
  * nf4_grad_a_plan -- host-only introspection of the launch plan nf4_grad_a
  * uses for a shape (no device work).  out5 receives, in order: kernel
- * (0 = tiled, 1 = skinny M <= 16, 2 = zero fill for N == 0), 32-row blocks
- * per wave of the tiled kernel, number of N-chunks (1 = no workspace), rows
- * per N-chunk, workgroups of the main launch.  Returns NF4_ERR_SHAPE /
- * NF4_ERR_NULL like nf4_grad_a.
+ * (0 = tiled, 1 = skinny M <= 16, 2 = zero fill for N == 0, 3 = wide tiled),
+ * the kernel's tile parameter (tiled: 32-row blocks per wave; wide: column
+ * groups of 128, the tile being 512 x 128 or 256 x 256), number of N-chunks
+ * (1 = no workspace), rows per N-chunk, workgroups of the main launch.
+ * Returns NF4_ERR_SHAPE / NF4_ERR_NULL like nf4_grad_a.
  */
 int nf4_grad_a_plan(int64_t M, int64_t N, int64_t K, int* out5);
 
 /*
  * nf4_grad_a_forced -- nf4_grad_a with the launch plan forced, for tests and
  * tuning: kernel 0 = tiled with `rb` (1 or 2) 32-row blocks per wave, kernel
- * 1 = skinny (requires M <= 16); `splits` = requested number of N-chunks
+ * 1 = skinny (requires M <= 16), kernel 3 = wide tiled with `rb` (1 or 2)
+ * column groups (requires N % 64 == 0 and grad_out and the codes below 2 GiB);
+ * `splits` = requested number of N-chunks
  * (rounded so that every chunk but the last is a whole number of stages).
  * Same contract and results-to-bound as nf4_grad_a; NF4_ERR_SHAPE if the
  * forced plan does not fit the shape.

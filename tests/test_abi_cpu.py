@@ -91,14 +91,23 @@ def test_plan_is_consistent(nb, M, N, K):
     if N == 0:
         assert p["kernel"] == "zero_fill"
         return
-    assert p["kernel"] == ("skinny" if M <= 16 else "tile")
+    if M <= 16:
+        assert p["kernel"] == "skinny"
+    else:
+        assert p["kernel"] in ("tile", "wide")
+    if p["kernel"] == "wide":  # only where the wide kernel's preconditions hold
+        assert N % 64 == 0 and M * N * 4 < 2 ** 31 and N * K // 2 < 2 ** 31
     assert p["splits"] >= 1
     assert p["n_chunk"] * p["splits"] >= N > p["n_chunk"] * (p["splits"] - 1)
     tiles_k = -(-K // 256)
     if p["kernel"] == "skinny":
         assert p["n_chunk"] % 128 == 0
         assert p["grid"] == tiles_k * p["splits"]
-    else:
+    elif p["kernel"] == "tile":
         assert p["n_chunk"] % 64 == 0
         bm = 128 * p["rb"]
         assert p["grid"] == -(-M // bm) * tiles_k * p["splits"]
+    else:
+        assert p["n_chunk"] % 64 == 0 and p["rb"] in (1, 2)
+        bm, bk = 512 // p["rb"], 128 * p["rb"]
+        assert p["grid"] == -(-M // bm) * -(-K // bk) * p["splits"]

@@ -159,6 +159,28 @@ def test_grad_a_tile_variants_ragged(lib, kernel, rb, splits, M, N, K):
                  what=f"{kernel} rb{rb} s{splits} {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("rb,splits", [(1, 1), (2, 1), (1, 3), (2, 2)])
+@pytest.mark.parametrize("M,N,K", [(17, 64, 64), (200, 384, 768), (513, 640, 320), (600, 1024, 448),
+                                   (1030, 256, 1088)])
+def test_grad_a_wide_variants_ragged(lib, rb, splits, M, N, K):
+    """Wide tile kernel (N % 64 == 0): 512x128 and 256x256 tiles, ragged M and K tails, N splits."""
+    g, s, b = random_inputs(M, N, K, seed=M + 7 * N + K + rb * 13 + splits)
+    check_grad_a(lib, g, s, b, M, N, K, kernel="wide", rb=rb, splits=splits,
+                 what=f"wide rb{rb} s{splits} {M}x{N}x{K}")
+
+
+def test_grad_a_wide_deterministic_and_rejects_ragged_n(lib):
+    M, N, K = 700, 4096, 384
+    g, s, b = random_inputs(M, N, K, seed=31)
+    gd, sd, bd = dev(g), dev(s), dev(b)
+    for rb, splits in [(1, 1), (2, 3)]:
+        r1 = host(lib.grad_a_forced(gd, sd, bd, "wide", rb=rb, splits=splits))
+        r2 = host(lib.grad_a_forced(gd, sd, bd, "wide", rb=rb, splits=splits))
+        assert np.array_equal(r1.view(np.uint32), r2.view(np.uint32))
+    with pytest.raises(lib.Nf4Error):
+        lib.grad_a_forced(dev(g[:, :4000]), sd[:4000], bd[:4000], "wide", rb=1)
+
+
 PAGE_SHAPES = [(128, 1536, 1536), (64, 256, 128), (16, 64, 64), (512, 1536, 1536), (512, 256, 1536),
                (512, 4608, 1536), (512, 1536, 4608)]
 
