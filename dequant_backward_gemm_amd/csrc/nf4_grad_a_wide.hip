@@ -40,9 +40,10 @@
 //   stage, k-step s, lane quarter q and element e is reduction row
 //   n = n0 + 32*s + 16*(e/4) + 4*q + e%4 for both operands (what the transpose
 //   of grad_out produces; consecutive pairs of n stay in one register).
-// * Table slots are permuted so that the 16 tables a wave instruction reads
-//   (random codes) fall in distinct 8-bank groups per half-wave; fragment
-//   writes and reads are lane-linear, so no access has bank conflicts.
+// * Table slots are permuted so that the tables a half-wave reads at once
+//   (random codes) fall in distinct 8-bank groups, and the decode lanes are
+//   assigned so that a half-wave's fragment stores are consecutive dwords:
+//   no LDS access has bank conflicts.
 //
 // Every global load is in bounds by clamping (rows of grad_out past M, code
 // columns past K, stages past the end of a chunk); such values only reach
@@ -68,11 +69,15 @@ struct WideCfg {
 };
 
 // Table slot (row n * KB + block) -> position in units of 32 bytes.  Slots are
-// permuted inside aligned groups of four so that the tables of the four row
-// pairs a half-wave reads at once sit in four different 8-bank groups.
+// permuted inside aligned groups of four so that the tables a half-wave reads
+// at once -- rows r, r + 2, r + 16, r + 18 of the stage at one block -- sit in
+// four different 8-bank groups (rows differing in bits 1 and 4 are rotated
+// apart).
 template <int KB>
 __device__ __forceinline__ uint32_t table_pos(uint32_t slot) {
-  return (slot & ~3u) | ((slot + slot / (2 * KB)) & 3u);
+  const uint32_t row = slot / KB;
+  const uint32_t g = ((row >> 1) & 1u) + 2u * ((row >> 4) & 1u);
+  return (slot & ~3u) | (((slot & 3u) + g) & 3u);
 }
 
 template <int WC>
@@ -119,9 +124,12 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
   const uint32_t rbase = Cfg::kFragBase + (uint32_t)wc * 8192u + 16u * lane;
 
   // ---- decode role: rows (nr0, nr0 + 1) of a stage, code dword 16*v + dl ----
-  // wave w covers stage rows 8w .. 8w+7 (k-step w/4, quarter w%4), lane pair p
+  // Wave w takes the 8 stage rows that fill lane quarter q = w%4 of k-step
+  // w/4 -- rows 16*(p/2) + 4q + 2*(p%2) (+1) of the k-step for its lane pair p,
+  // which are B-operand register p -- so that a half-wave's fragment stores
+  // are 32 consecutive dwords.
   const int p = lane & 3, dl = lane >> 2;
-  const int nr0 = 8 * wave + 2 * p;
+  const int nr0 = 32 * (wave >> 2) + 16 * (p >> 1) + 4 * (wave & 3) + 2 * (p & 1);
   // Code columns past K (last tile) read the next row, or zero past the end of
   // the array; they only reach columns that are never stored.
   const uint32_t cvoff = (uint32_t)nr0 * crow + (uint32_t)(k0 / 2 + 4 * dl);
@@ -135,11 +143,9 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
     }
   }
   // fragment dword written for column c of code dword 16*v + dl: k-step wave/4,
-  // group v, tile c; the rows' place n % 32 = 8*(wave%4) + 2p in the k-step is
-  // lane quarter (n % 16) / 4, register 2*(n / 16) + (n % 4) / 2
+  // group v, tile c, lane dl + 16*(wave%4), register p
   const uint32_t wb = Cfg::kFragBase + (uint32_t)(wave >> 2) * WC * 8192u +
-                      (uint32_t)(dl + 16 * (2 * (wave & 1) + (p >> 1))) * 16u +
-                      4u * (uint32_t)(2 * ((wave >> 1) & 1) + (p & 1));
+                      (uint32_t)(dl + 16 * (wave & 3)) * 16u + 4u * (uint32_t)p;
 
   // ---- table role: slot (tid / 4) + 128 * u, levels 4 * (tid % 4) .. + 3 ----
   // (slot + 128 is row + 128 / KB of the same block, and its table sits 4 KiB
