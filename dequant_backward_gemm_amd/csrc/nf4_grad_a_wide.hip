@@ -204,13 +204,14 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
   // l1 l0 = chunk bits C1 C0, v0 = C2, (l3 l2 v2 v1) = row bits R3..R0 and
   // l5 l4 = R5 R4.  Exchanging l0 <-> v1, l1 <-> v2, l4 <-> v1, l5 <-> v2 gives
   // lane = (C1 C0 R3 R2 R1 R0) = (q, i) and v = (R5 R4 C2) = (row block, half).
-  auto to_a_frags = [&](const float (&a)[8][4], u32x4 (&af)[4]) {
-    uint32_t r[8][2];
+  auto round_a = [&](const float (&a)[8][4], uint32_t (&r)[8][2]) {
 #pragma unroll
     for (int v = 0; v < 8; ++v) {
       r[v][0] = pack_half2_rne(a[v][0], a[v][1]);
       r[v][1] = pack_half2_rne(a[v][2], a[v][3]);
     }
+  };
+  auto to_a_frags = [&](uint32_t (&r)[8][2], u32x4 (&af)[4]) {
 #pragma unroll
     for (int g = 0; g < 2; ++g) {  // l0 <-> v1: pairs (v, v + 2), v in {4g, 4g + 1}
       uint32_t lo[4] = {r[4 * g][0], r[4 * g][1], r[4 * g + 1][0], r[4 * g + 1][1]};
@@ -322,10 +323,16 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
     for_each_index(std::make_integer_sequence<int, 2>{}, [&](auto sc_) {
       constexpr int s = decltype(sc_)::value;
       constexpr int c0 = 4 * s;  // decode columns c0 .. c0 + 3 in this k-step
-      u32x4 af[4];
-      to_a_frags(ar, af);
-      __builtin_amdgcn_sched_barrier(0);  // transpose temporaries die before the next loads' registers
+      // round this k-step's grad_out (freeing the load registers), issue the
+      // next k-step's loads, then transpose: the loads do not wait for the
+      // transpose, and its temporaries never coexist with the raw values
+      uint32_t rr[8][2];
+      round_a(ar, rr);
+      __builtin_amdgcn_sched_barrier(0);
       load_a(s == 0 ? st : st + 1, s ^ 1, ar);
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4 af[4];
+      to_a_frags(rr, af);
       auto read_b = [&](int t) { return lds_load_u32x4(smem, rbase + frd + (uint32_t)((s * WC * 8 + t) * 1024)); };
       u32x4 bf[3];
       bf[0] = read_b(0);
