@@ -315,7 +315,7 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
     prep(xc);
     // k-step s: convert grad_out of s and issue the loads of the next k-step,
     // then 8 ticks, one per MFMA tile t (4 MFMAs, one per row block).  B
-    // fragments are read two ticks ahead through a ring of three; the decode
+    // fragments are read three ticks ahead through a ring of four; the decode
     // of columns 4s .. 4s+3 of the next stage (table reads, then two ticks
     // later the pack and fragment store) and the per-stage extras are spread
     // over the ticks.  Scheduling barriers between ticks keep every load where
@@ -334,17 +334,18 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
       u32x4 af[4];
       to_a_frags(rr, af);
       auto read_b = [&](int t) { return lds_load_u32x4(smem, rbase + frd + (uint32_t)((s * WC * 8 + t) * 1024)); };
-      u32x4 bf[3];
+      u32x4 bf[4];
       bf[0] = read_b(0);
       bf[1] = read_b(1);
+      bf[2] = read_b(2);
       uint32_t lk[2][WC][2];
       __builtin_amdgcn_sched_barrier(0);
       for_each_index(std::make_integer_sequence<int, 8>{}, [&](auto tc) {
         constexpr int t = decltype(tc)::value;
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
-          acc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(af[rb]), as_half8(bf[t % 3]), acc[rb][t], 0, 0, 0);
-        if constexpr (t + 2 < 8) bf[(t + 2) % 3] = read_b(t + 2);
+          acc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(af[rb]), as_half8(bf[t % 4]), acc[rb][t], 0, 0, 0);
+        if constexpr (t + 3 < 8) bf[(t + 3) % 4] = read_b(t + 3);
         if constexpr (t >= 2 && t < 6) store_col(std::integral_constant<int, c0 + t - 2>{}, fwr, lk[t & 1]);
         if constexpr (t < 4) lookup_col(std::integral_constant<int, c0 + t>{}, toff_dec, lk[t & 1]);
         if constexpr (t == 6 && s == 0) load_codes(st + 2, xn);
