@@ -90,19 +90,29 @@ def run_step(nb, weights, gouts, outs, events=None):
                 nb.grad_a(gouts[p], s, c, out=outs[p])
 
 
-def kernel_name_for(plan):
+def kernel_name_for(plan, N=None):
+    """Name (as rocprofv3 reports it, without namespace and arguments) of the main kernel a plan launches."""
     if plan["kernel"] == "skinny":
         return "grad_a_skinny_kernel"
     if plan["kernel"] == "zero_fill":
         return "fill_zero_kernel"
+    if plan["kernel"] == "wide":
+        return "grad_a_wide_kernel<%d>" % plan["rb"]
+    if plan["rb"] == 2 and N is not None and N % 64 == 0:
+        return "grad_a_tile_fast_kernel"
     return "grad_a_tile_kernel<%d>" % plan["rb"]
+
+
+# Device code of the grad_A kernels; a recorded counter summary is valid only
+# for the sources it was taken on.
+KERNEL_SOURCES = ("nf4_grad_a.hip", "nf4_grad_a_wide.hip", "nf4_kernel_util.h", "nf4_device.h")
 
 
 def source_digest():
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
-    for f in ("nf4_grad_a.hip", "nf4_device.h"):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(here, "dequant_backward_gemm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -213,7 +223,7 @@ def cpu_baseline():
     import numpy as np
     import oracle
     import synth
-    rows = 256
+    rows = 3072  # about 10-15 s of fp64 CPU work on the 16-core host share
     flops = 0.0
     t = 0.0
     for pi, (p, N, K) in enumerate(PROJ):
@@ -293,7 +303,7 @@ def main():
     by_kernel = {}
     for p, a, b in events["done"]:
         N, K = shapes[p]
-        name = kernel_name_for(nb.grad_a_plan(M_STEP, N, K))
+        name = kernel_name_for(nb.grad_a_plan(M_STEP, N, K), N)
         d = by_kernel.setdefault(name, [0.0, 0.0, 0])
         d[0] += a.elapsed_time(b) * 1e-3
         d[1] += 2.0 * M_STEP * N * K

@@ -620,183 +620,34 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(floatx4* __restrict__ ou
 }
 
 // ---------------------------------------------------------------------------
-// Host dispatch
+// Launchers (called by the planner in nf4_plan.hip)
 // ---------------------------------------------------------------------------
-static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-constexpr int kCUs = 256;
-
-GradAPlan plan_grad_a(int64_t M, int64_t N, int64_t K) {
-  GradAPlan p{};
-  if (N == 0) {
-    p.kernel = 2;
-    p.splits = 1;
-    p.n_chunk = 0;
-    p.grid = (int)std::min<int64_t>(cdiv(M * K / 4, 256), 4096);
-    return p;
-  }
-  const int64_t tiles_k = cdiv(K, 256);
-  if (M <= 16) {
-    // Each workgroup streams one 256-wide column strip over an N-chunk
-    // (multiple of 128 rows).  Aim for ~4 workgroups per CU while keeping the
-    // fp32 partials (M*K per chunk) small next to the code bytes streamed.
-    p.kernel = 1;
-    p.rb = 0;
-    int64_t want = cdiv(4 * kCUs, tiles_k);
-    const int64_t part_cap = std::max<int64_t>(1, (N * K / 2) / (20 * 4 * M * K));  // partials <= 5%
-    int64_t splits = std::max<int64_t>(1, std::min(want, std::max<int64_t>(part_cap, cdiv(kCUs, tiles_k))));
-    splits = std::min(splits, cdiv(N, 128));
-    int64_t chunk = cdiv(cdiv(N, splits), 128) * 128;
-    splits = cdiv(N, chunk);
-    p.splits = (int)splits;
-    p.n_chunk = (int)chunk;
-    p.grid = (int)(tiles_k * splits);
-    return p;
-  }
-  // Tile kernels: pick the kernel, its tile and the N split by a simple cost
-  // model: wave-quantised MFMA time at a measured efficiency plus the
-  // partial-sum traffic of a split.
-  const double cu_rate = 4096.0 * 2.4e9;  // fp16 MFMA flop/s per CU
-  double best = 1e30;
-  // Splitting N pays only when the tiles alone leave most CUs idle: measured
-  // with the wide kernel, 48 tiles ran 9% faster split in two and 96 tiles 33%
-  // slower (partials, the reduce launch and cache pressure).  Problems under a
-  // GFLOP are launch-bound and never split.
-  const bool tiny = 2.0 * (double)M * (double)N * (double)K < 1e9;
-  auto consider = [&](int kernel, int param, int64_t BM, int64_t BK, int per_cu, double eff) {
-    const int64_t tiles = cdiv(M, BM) * cdiv(K, BK);
-    const int64_t max_split = (tiny || tiles >= 64) ? 1 : cdiv(N, 64);
-    for (int64_t s = 1; s <= std::min<int64_t>(max_split, 16); ++s) {
-      const int64_t chunk = cdiv(cdiv(N, s), 64) * 64;
-      const int64_t se = cdiv(N, chunk);
-      if (se != s) continue;
-      const int64_t units = tiles * se;
-      const int64_t rounds = cdiv(units, (int64_t)kCUs * per_cu);
-      const double t_unit = (double)BM * (double)BK * (double)chunk * 2.0 / (cu_rate * eff / per_cu);
-      double t = (double)rounds * t_unit + 3e-6;
-      // split partials: written once and read once by the reduce kernel (measured ~2.5 TB/s
-      // effective), plus the extra launch
-      if (se > 1) t += 2.0 * (double)se * (double)M * (double)K * 4.0 / 2.5e12 + 8e-6;
-      if (t < best * 0.999) {
-        best = t;
-        p.kernel = kernel;
-        p.rb = param;
-        p.splits = (int)se;
-        p.n_chunk = (int)chunk;
-        p.grid = (int)units;
-      }
-    }
-  };
-  // measured on MI355X (fraction of the fp16 MFMA rate at M = 8192): tile
-  // kernel with 128-row tiles (two workgroups per CU) ~0.24, 256-row tiles
-  // ~0.19; wide kernel 512 x 128 tiles ~0.28, 256 x 256 tiles ~0.11
-  consider(0, 2, 256, 256, 1, 0.19);
-  consider(0, 1, 128, 256, 2, 0.24);
-  if (wide_kernel_supported(M, N, K)) {
-    consider(3, 1, wide_tile_rows(1), wide_tile_cols(1), 1, 0.28);
-    consider(3, 2, wide_tile_rows(2), wide_tile_cols(2), 1, 0.11);
-  }
-  return p;
+hipError_t launch_grad_a_tile(int rb, bool fast, int grid, const float* grad_out, const float* scales,
+                              const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,
+                              int tiles_k, hipStream_t stream) {
+  // the fast kernel has a fixed 256-row tile
+  auto kern = (fast && rb == 2) ? grad_a_tile_fast_kernel : (rb == 2 ? grad_a_tile_kernel<2> : grad_a_tile_kernel<1>);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, grad_out, scales, codes, dst, M, N, K, n_chunk, tiles_m,
+                     tiles_k);
+  return hipGetLastError();
 }
 
-bool make_plan(int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, GradAPlan* out) {
-  GradAPlan p{};
-  if (N == 0) {
-    *out = plan_grad_a(M, N, K);
-    return true;
-  }
-  if (splits < 1 || splits > 4096) return false;
-  const int64_t tiles_k = cdiv(K, 256);
-  if (kernel == 1) {
-    if (M > 16) return false;
-    const int64_t chunk = cdiv(cdiv(N, splits), 128) * 128;
-    p.kernel = 1;
-    p.rb = 0;
-    p.n_chunk = (int)chunk;
-    p.splits = (int)cdiv(N, chunk);
-    p.grid = (int)(tiles_k * p.splits);
-  } else if (kernel == 0) {
-    if (rb != 1 && rb != 2) return false;
-    const int64_t chunk = cdiv(cdiv(N, splits), 64) * 64;
-    p.kernel = 0;
-    p.rb = rb;
-    p.n_chunk = (int)chunk;
-    p.splits = (int)cdiv(N, chunk);
-    p.grid = (int)(cdiv(M, 128 * rb) * tiles_k * p.splits);
-  } else if (kernel == 3) {
-    if ((rb != 1 && rb != 2) || !wide_kernel_supported(M, N, K)) return false;
-    const int64_t chunk = cdiv(cdiv(N, splits), 64) * 64;
-    p.kernel = 3;
-    p.rb = rb;
-    p.n_chunk = (int)chunk;
-    p.splits = (int)cdiv(N, chunk);
-    p.grid = (int)(cdiv(M, wide_tile_rows(rb)) * cdiv(K, wide_tile_cols(rb)) * p.splits);
-  } else {
-    return false;
-  }
-  *out = p;
-  return true;
+hipError_t launch_grad_a_skinny(int grid, const float* grad_out, const float* scales, const uint32_t* codes,
+                                float* dst, int M, int N, int K, int n_chunk, int tiles_k, hipStream_t stream) {
+  hipLaunchKernelGGL(grad_a_skinny_kernel, dim3(grid), dim3(256), 0, stream, grad_out, scales, codes, dst, M, N, K,
+                     n_chunk, tiles_k);
+  return hipGetLastError();
 }
 
-hipError_t launch_grad_a(const float* grad_out, const float* scales, const uint8_t* codes, float* grad_a,
-                         int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  return launch_grad_a_plan(plan_grad_a(M, N, K), grad_out, scales, codes, grad_a, M, N, K, stream);
+hipError_t launch_grad_a_reduce(int grid, const float* ws, float* out, int64_t n4, int splits, hipStream_t stream) {
+  hipLaunchKernelGGL(grad_a_reduce_kernel, dim3(grid), dim3(256), 0, stream, reinterpret_cast<const floatx4*>(ws),
+                     reinterpret_cast<floatx4*>(out), n4, splits);
+  return hipGetLastError();
 }
 
-hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const float* scales, const uint8_t* codes,
-                              float* grad_a, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  const uint32_t* c32 = reinterpret_cast<const uint32_t*>(codes);
-  if (p.kernel == 2) {
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(p.grid), dim3(256), 0, stream, reinterpret_cast<floatx4*>(grad_a),
-                       M * K / 4);
-    return hipGetLastError();
-  }
-  float* dst = grad_a;
-  float* ws = nullptr;
-  if (p.splits > 1) {
-    const size_t bytes = (size_t)p.splits * (size_t)M * (size_t)K * sizeof(float);
-    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&ws), bytes, stream);
-    if (e != hipSuccess) return e;
-    dst = ws;
-  }
-  const int tiles_k = (int)cdiv(K, 256);
-  if (p.kernel == 1) {
-    hipLaunchKernelGGL(grad_a_skinny_kernel, dim3(p.grid), dim3(256), 0, stream, grad_out, scales, c32, dst, (int)M,
-                       (int)N, (int)K, p.n_chunk, tiles_k);
-  } else if (p.kernel == 3) {
-    const hipError_t e = launch_grad_a_wide(p.rb, p.grid, grad_out, scales, c32, dst, (int)M, (int)N, (int)K,
-                                            p.n_chunk, (int)cdiv(M, wide_tile_rows(p.rb)),
-                                            (int)cdiv(K, wide_tile_cols(p.rb)), stream);
-    if (e != hipSuccess) {
-      if (ws) (void)hipFreeAsync(ws, stream);
-      return e;
-    }
-  } else {
-    const int tiles_m = (int)cdiv(M, 128 * p.rb);
-    // fast path: every stage of every chunk is full and every array has 32-bit byte offsets
-    const bool fast = (N % 64) == 0 && (uint64_t)M * (uint64_t)N * 4 < (1ull << 31) &&
-                      (uint64_t)N * (uint64_t)K / 2 < (1ull << 31);
-    // the fast kernel has a fixed 256-row tile
-    auto kern = (fast && p.rb == 2) ? grad_a_tile_fast_kernel
-                                    : (p.rb == 2 ? grad_a_tile_kernel<2> : grad_a_tile_kernel<1>);
-    hipLaunchKernelGGL(kern, dim3(p.grid), dim3(256), 0, stream, grad_out, scales, c32, dst, (int)M, (int)N, (int)K,
-                       p.n_chunk, tiles_m, tiles_k);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) {
-    if (ws) (void)hipFreeAsync(ws, stream);
-    return e;
-  }
-  if (p.splits > 1) {
-    const int64_t n4 = M * K / 4;
-    const int grid = (int)std::min<int64_t>(cdiv(n4, 256), 8192);
-    hipLaunchKernelGGL(grad_a_reduce_kernel, dim3(grid), dim3(256), 0, stream, reinterpret_cast<const floatx4*>(ws),
-                       reinterpret_cast<floatx4*>(grad_a), n4, p.splits);
-    e = hipGetLastError();
-    hipError_t f = hipFreeAsync(ws, stream);
-    if (e == hipSuccess) e = f;
-  }
-  return e;
+hipError_t launch_fill_zero(int grid, float* out, int64_t n4, hipStream_t stream) {
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, stream, reinterpret_cast<floatx4*>(out), n4);
+  return hipGetLastError();
 }
 
 }  // namespace nf4

@@ -47,4 +47,13 @@ hipError_t launch_grad_a_wide(int wc, int grid, const float* grad_out, const flo
                               float* dst, int M, int N, int K, int n_chunk, int tiles_m, int tiles_k,
                               hipStream_t stream);
 
+// Kernel launchers of nf4_grad_a.hip (tile, skinny, split reduction, zero fill).
+hipError_t launch_grad_a_tile(int rb, bool fast, int grid, const float* grad_out, const float* scales,
+                              const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,
+                              int tiles_k, hipStream_t stream);
+hipError_t launch_grad_a_skinny(int grid, const float* grad_out, const float* scales, const uint32_t* codes,
+                                float* dst, int M, int N, int K, int n_chunk, int tiles_k, hipStream_t stream);
+hipError_t launch_grad_a_reduce(int grid, const float* ws, float* out, int64_t n4, int splits, hipStream_t stream);
+hipError_t launch_fill_zero(int grid, float* out, int64_t n4, hipStream_t stream);
+
 }  // namespace nf4
