@@ -1,0 +1,242 @@
+// Streaming kernel for grad_A = grad_out . dequant(W) with 1 <= M <= 16.
+//
+// Same arithmetic as the other grad_A kernels (grad_out rounded fp32 -> fp16,
+// weights fp16(fl32(scale * level)), fp16 MFMA products accumulated in fp32
+// over N).  At this size the work is streaming the packed weight once, so the
+// kernel is organised for HBM bandwidth and decode throughput:
+//
+// * A workgroup (8 waves) owns a 128-column strip of grad_A over an N-chunk;
+//   the waves take interleaved k-steps of 32 rows of N and are summed in a
+//   fixed order at the end (LDS), the N-chunks by the split reduction.
+// * Per k-step a wave builds the fp16 weight tables of its 32 rows x 2 scale
+//   blocks in its own LDS area -- the 16 values fp16(fl32(scale * level)) a
+//   code can stand for -- then decodes every weight with one 16-bit table
+//   read straight into its MFMA B operands (no fragment round trip: every
+//   decoded weight is used by this wave only).
+// * MFMA 16x16x32 with grad_out rows padded to 16 (rows >= M read as zero).
+//   B lane (c, q) holds rows n0 + 8q + e (e = 0..7) at column k0 + 8c + t of
+//   tile t, so a lane's 8 columns are one code dword per row and the 8 tiles
+//   give each lane 8 consecutive outputs per row.
+// * grad_out is loaded with four lanes per 128-byte line (one row's 32
+//   values of the k-step), rounded to fp16 and moved into the A layout (one
+//   row per lane) through a 1 KiB per-wave LDS slot.
+//
+// N tails and chunk ends: rows n >= chunk end get scale 0 (so every table
+// entry, hence every decoded weight, is +-0) and grad_out 0; code rows past
+// the array read zero through the buffer range check.  Columns past K only
+// reach outputs that are not stored.
+#include "nf4_kernel_util.h"
+#include "nf4_launch.h"
+
+namespace nf4 {
+
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyBK = 128;
+// Per-wave LDS in the loop: tables (4 groups of 8 rows x 2 blocks x 32 B, each
+// group padded by 64 B so that the groups a half-wave reads sit 64 B apart in
+// the bank space), then the grad_out staging slot.
+constexpr int kSkTabGroup = 8 * 2 * 32 + 64;          // 576
+constexpr int kSkTabBytes = 4 * kSkTabGroup;          // 2304
+constexpr int kSkWaveBytes = kSkTabBytes + 1024;      // + A staging
+constexpr int kSkRedBytes = kSkinnyWaves * 16 * kSkinnyBK * 4;  // 64 KiB reduction buffer
+static_assert(kSkinnyWaves * kSkWaveBytes <= kSkRedBytes, "loop LDS fits in the reduction buffer");
+
+template <bool VEC_A>
+__global__ __launch_bounds__(512, 2) void grad_a_stream_kernel(const float* __restrict__ G,
+                                                               const float* __restrict__ S,
+                                                               const uint32_t* __restrict__ C32,
+                                                               float* __restrict__ out, int M, int N, int K,
+                                                               int n_chunk, int tiles_k) {
+  __shared__ __attribute__((aligned(16))) uint32_t smem[kSkRedBytes / 4];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int ci = lane & 15, q = lane >> 4;
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int kt = logical % tiles_k;
+  const int split = logical / tiles_k;
+  const int k0 = kt * kSkinnyBK;
+  const int nb = split * n_chunk;
+  const int ne = min(N, nb + n_chunk);
+  const int nsteps = (ne - nb + 31) >> 5;
+
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(C32, (uint32_t)((size_t)N * (size_t)K / 2));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, (uint32_t)((size_t)N * (size_t)(K / 64) * 4));
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(G, (uint32_t)((size_t)M * (size_t)N * 4));
+  const uint32_t crow = (uint32_t)K / 2;   // bytes per code row
+  const uint32_t srow = (uint32_t)K / 16;  // bytes per scale row
+
+  const uint32_t wbase = (uint32_t)wave * kSkWaveBytes;
+  // code dword of lane (ci, q): rows n0 + 8q + e, columns k0 + 8ci .. + 7
+  const uint32_t cvoff = 8u * q * crow + (uint32_t)(k0 / 2 + 4 * ci);
+  // table reads of lane (ci, q): group q, block ci / 8, row e at +64e, code c at +2c
+  const uint32_t tlook = wbase + (uint32_t)q * kSkTabGroup + 32u * (uint32_t)(ci >> 3);
+  // table built by lane L: row L / 2 (group (L/2)/8, row (L/2)%8), block L % 2
+  const int trow = lane >> 1, tkb = lane & 1;
+  const uint32_t tbuild = wbase + (uint32_t)(trow >> 3) * kSkTabGroup + 64u * (trow & 7) + 32u * tkb;
+  const uint32_t svoff = (uint32_t)trow * srow + 4u * (uint32_t)(k0 / 64 + tkb);
+  // grad_out as loaded by lane L: row L / 4, values 8 * (L % 4) .. + 7 of the k-step;
+  // staged at the A-operand slot of lane 16 * (L % 4) + L / 4
+  const int arow = lane >> 2, aq = lane & 3;
+  // rows >= M read through an offset past the buffer's range: zero, no memory traffic
+  const uint32_t avoff = (arow < M) ? (uint32_t)arow * (uint32_t)N * 4u + 32u * aq : 0x80000000u;
+  const uint32_t astore = wbase + kSkTabBytes + 16u * (uint32_t)(16 * aq + arow);
+  const uint32_t aread = wbase + kSkTabBytes + 16u * (uint32_t)lane;
+
+  floatx4 acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  struct Step {
+    uint32_t x[8];
+    float sc;
+    float a[8];
+  };
+  // (k-steps past the chunk are clamped to its last one: the loads stay
+  // unconditional, so the wait counts never depend on a branch)
+  auto load_step = [&](int j, Step& d) {
+    const uint32_t n0 = (uint32_t)(nb + 32 * min(j, nsteps - 1));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d.x[e] = __builtin_amdgcn_raw_buffer_load_b32(rc, cvoff, (n0 + e) * crow, 0);
+    d.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, svoff, n0 * srow, 0));
+    if constexpr (VEC_A) {
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const floatx4 g4 =
+            __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rg, avoff + 16u * v, n0 * 4u, 0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d.a[4 * v + i] = g4[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        d.a[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, avoff + 4u * i, n0 * 4u, 0));
+    }
+  };
+
+  auto run_step = [&](int j, const Step& d) {
+    const int n0 = nb + 32 * j;
+    // tables of this k-step (rows past the chunk get scale 0)
+    {
+      const float sc = (n0 + trow < ne) ? d.sc : 0.f;
+      u32x4 w0, w1;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        w0[c] = pack_half2_rne(sc * kLevels[2 * c], sc * kLevels[2 * c + 1]);
+        w1[c] = pack_half2_rne(sc * kLevels[8 + 2 * c], sc * kLevels[8 + 2 * c + 1]);
+      }
+      lds_store_u32x4(smem, tbuild, w0);
+      lds_store_u32x4(smem, tbuild + 16u, w1);
+    }
+    // grad_out of the k-step into the A layout
+    u32x4 af;
+    {
+      const int nl = n0 + 8 * aq;
+      float g[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) g[i] = (nl + i < ne) ? d.a[i] : 0.f;
+      u32x4 h;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) h[p] = pack_half2_rne(g[2 * p], g[2 * p + 1]);
+      lds_store_u32x4(smem, astore, h);
+      af = lds_load_u32x4(smem, aread);
+    }
+    // decode (one table read per weight) and MFMA, tile by tile
+    uint32_t y[8], z[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      y[e] = (d.x[e] << 1) & 0x1E1E1E1Eu;
+      z[e] = (d.x[e] >> 3) & 0x1E1E1E1Eu;
+    }
+    // table reads of tile t + 1 are issued before tile t's are packed
+    uint32_t lk[2][8];
+    auto lookup = [&](auto tc, uint32_t (&l)[8]) {
+      constexpr int t = decltype(tc)::value;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        l[e] = lds_load_u16(smem, add_byte<(t >> 1)>(tlook, (t & 1) ? z[e] : y[e]) + 64u * e);
+    };
+    lookup(std::integral_constant<int, 0>{}, lk[0]);
+    for_each_index(std::make_integer_sequence<int, 8>{}, [&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      if constexpr (t + 1 < 8) lookup(std::integral_constant<int, t + 1>{}, lk[(t + 1) & 1]);
+      u32x4 b;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) b[p] = lk[t & 1][2 * p] | (lk[t & 1][2 * p + 1] << 16);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(af), as_half8(b), acc[t], 0, 0, 0);
+    });
+  };
+
+  // Wave w takes k-steps w, w + 8, ... (cnt of them); the next one's loads are
+  // in flight while one is decoded.  Two named buffers, a counted loop unrolled
+  // twice whose body is one basic block: no loop-carried copy of a register a
+  // load may still be writing (such a copy waits for the load), and no load
+  // batch interleaved with another.
+  const int cnt = (nsteps > wave) ? (nsteps - wave + kSkinnyWaves - 1) / kSkinnyWaves : 0;
+  if (cnt > 0) {
+    Step s0, s1;
+    auto jj = [&](int i) { return wave + kSkinnyWaves * i; };
+    load_step(jj(0), s0);
+    int i = 0;
+    for (; i + 2 <= cnt; i += 2) {
+      load_step(jj(i + 1), s1);
+      __builtin_amdgcn_sched_barrier(0);
+      run_step(jj(i), s0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_step(jj(i + 2), s0);
+      __builtin_amdgcn_sched_barrier(0);
+      run_step(jj(i + 1), s1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (i < cnt) run_step(jj(i), s0);
+  }
+
+  // fixed-order sum of the 8 waves: ((w0 + w1) + w2) + ... + w7
+  __syncthreads();
+  {
+    // accumulator lane (ci, q), register r: row 4q + r, columns 8ci + t
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const floatx4 lo = {acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+      const floatx4 hi = {acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
+      lds_store_u32x4(smem, (uint32_t)((wave * 16 + 4 * q + r) * kSkinnyBK + 8 * ci) * 4u,
+                      __builtin_bit_cast(u32x4, lo));
+      lds_store_u32x4(smem, (uint32_t)((wave * 16 + 4 * q + r) * kSkinnyBK + 8 * ci + 4) * 4u,
+                      __builtin_bit_cast(u32x4, hi));
+    }
+  }
+  __syncthreads();
+  {
+    const int row = tid >> 5, c4 = tid & 31;  // 16 rows x 32 float4
+    floatx4 s = __builtin_bit_cast(floatx4, lds_load_u32x4(smem, (uint32_t)(row * kSkinnyBK + 4 * c4) * 4u));
+#pragma unroll
+    for (int w = 1; w < kSkinnyWaves; ++w)
+      s += __builtin_bit_cast(floatx4,
+                              lds_load_u32x4(smem, (uint32_t)((w * 16 + row) * kSkinnyBK + 4 * c4) * 4u));
+    const int col = k0 + 4 * c4;
+    if (row < M && col < K) {
+      float* dst = out + (size_t)split * (size_t)M * (size_t)K;
+      *reinterpret_cast<floatx4*>(dst + (size_t)row * (size_t)K + col) = s;
+    }
+  }
+}
+
+bool stream_kernel_supported(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && M <= 16 && N > 0 && (uint64_t)M * (uint64_t)N * 4 < (1ull << 31) &&
+         (uint64_t)N * (uint64_t)K / 2 < (1ull << 31);
+}
+
+hipError_t launch_grad_a_stream(int grid, const float* grad_out, const float* scales, const uint32_t* codes,
+                                float* dst, int M, int N, int K, int n_chunk, int tiles_k, hipStream_t stream) {
+  if ((N & 3) == 0)
+    hipLaunchKernelGGL(grad_a_stream_kernel<true>, dim3(grid), dim3(512), 0, stream, grad_out, scales, codes, dst, M,
+                       N, K, n_chunk, tiles_k);
+  else
+    hipLaunchKernelGGL(grad_a_stream_kernel<false>, dim3(grid), dim3(512), 0, stream, grad_out, scales, codes, dst,
+                       M, N, K, n_chunk, tiles_k);
+  return hipGetLastError();
+}
+
+}  // namespace nf4

@@ -22,7 +22,7 @@ hipError_t launch_grad_a(const float* grad_out, const float* scales, const uint8
 // Launch plan chosen for a shape (exposed for tests and the benchmark).
 struct GradAPlan {
   int kernel;    // 0 = tile (BM = 128 * rb), 1 = skinny (M <= 16), 2 = zero-fill (N == 0),
-                 // 3 = wide (8 waves, tile (512 / rb) x (128 * rb))
+                 // 3 = wide (8 waves, tile (512 / rb) x (128 * rb)), 4 = stream (M <= 16)
   int rb;        // tile: 32-row blocks per wave; wide: 128-column groups
   int splits;    // number of N-chunks (1 = no workspace, no reduce launch)
   int n_chunk;   // rows of N per chunk
@@ -46,6 +46,13 @@ int wide_tile_cols(int wc);
 hipError_t launch_grad_a_wide(int wc, int grid, const float* grad_out, const float* scales, const uint32_t* codes,
                               float* dst, int M, int N, int K, int n_chunk, int tiles_m, int tiles_k,
                               hipStream_t stream);
+
+// Streaming kernel for M <= 16 (nf4_grad_a_skinny.hip): 128-column strips,
+// N-chunks of whole 32-row k-steps; needs 32-bit byte offsets.
+constexpr int kStreamBK = 128;
+bool stream_kernel_supported(int64_t M, int64_t N, int64_t K);
+hipError_t launch_grad_a_stream(int grid, const float* grad_out, const float* scales, const uint32_t* codes,
+                                float* dst, int M, int N, int K, int n_chunk, int tiles_k, hipStream_t stream);
 
 // Kernel launchers of nf4_grad_a.hip (tile, skinny, split reduction, zero fill).
 hipError_t launch_grad_a_tile(int rb, bool fast, int grid, const float* grad_out, const float* scales,

@@ -21,6 +21,33 @@ GradAPlan plan_grad_a(int64_t M, int64_t N, int64_t K) {
     return p;
   }
   const int64_t tiles_k = cdiv(K, 256);
+  if (M <= 16 && stream_kernel_supported(M, N, K)) {
+    // Streaming kernel: 128-column strips x N-chunks.  Pick the chunk count by
+    // a bandwidth model: the weight stream runs at the chip rate once about
+    // two workgroups per CU are resident; a split adds its partials (written
+    // and read once) and the reduce launch.
+    const int64_t tk = cdiv(K, kStreamBK);
+    const double bw = 5.0e12;
+    const double stream_bytes = (double)N * (double)K * (0.5 + 1.0 / 16.0) + 4.0 * (double)M * (double)(N + K);
+    double best = 1e30;
+    for (int64_t s = 1; s <= 64; ++s) {
+      const int64_t chunk = cdiv(cdiv(N, s), 32) * 32;
+      const int64_t se = cdiv(N, chunk);
+      if (se != s) continue;
+      const double occ = std::min(1.0, (double)(tk * se) / (2.0 * kCUs));
+      double t = stream_bytes / (bw * occ) + 3e-6;
+      if (se > 1) t += 2.0 * (double)se * (double)M * (double)K * 4.0 / bw + 6e-6;
+      if (t < best * 0.999) {
+        best = t;
+        p.kernel = 4;
+        p.rb = 0;
+        p.splits = (int)se;
+        p.n_chunk = (int)chunk;
+        p.grid = (int)(tk * se);
+      }
+    }
+    return p;
+  }
   if (M <= 16) {
     // Each workgroup streams one 256-wide column strip over an N-chunk
     // (multiple of 128 rows).  Aim for ~4 workgroups per CU while keeping the
@@ -108,6 +135,14 @@ bool make_plan(int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, 
     p.n_chunk = (int)chunk;
     p.splits = (int)cdiv(N, chunk);
     p.grid = (int)(cdiv(M, 128 * rb) * tiles_k * p.splits);
+  } else if (kernel == 4) {
+    if (!stream_kernel_supported(M, N, K)) return false;
+    const int64_t chunk = cdiv(cdiv(N, splits), 32) * 32;
+    p.kernel = 4;
+    p.rb = 0;
+    p.n_chunk = (int)chunk;
+    p.splits = (int)cdiv(N, chunk);
+    p.grid = (int)(cdiv(K, kStreamBK) * p.splits);
   } else if (kernel == 3) {
     if ((rb != 1 && rb != 2) || !wide_kernel_supported(M, N, K)) return false;
     const int64_t chunk = cdiv(cdiv(N, splits), 64) * 64;
@@ -144,6 +179,9 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
   hipError_t e = hipSuccess;
   if (p.kernel == 1) {
     e = launch_grad_a_skinny(p.grid, grad_out, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk, tiles_k, stream);
+  } else if (p.kernel == 4) {
+    e = launch_grad_a_stream(p.grid, grad_out, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
+                             (int)cdiv(K, kStreamBK), stream);
   } else if (p.kernel == 3) {
     e = launch_grad_a_wide(p.rb, p.grid, grad_out, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
                            (int)cdiv(M, wide_tile_rows(p.rb)), (int)cdiv(K, wide_tile_cols(p.rb)), stream);

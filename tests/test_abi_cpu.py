@@ -92,7 +92,7 @@ def test_plan_is_consistent(nb, M, N, K):
         assert p["kernel"] == "zero_fill"
         return
     if M <= 16:
-        assert p["kernel"] == "skinny"
+        assert p["kernel"] in ("skinny", "stream")
     else:
         assert p["kernel"] in ("tile", "wide")
     if p["kernel"] == "wide":  # only where the wide kernel's preconditions hold
@@ -103,6 +103,9 @@ def test_plan_is_consistent(nb, M, N, K):
     if p["kernel"] == "skinny":
         assert p["n_chunk"] % 128 == 0
         assert p["grid"] == tiles_k * p["splits"]
+    elif p["kernel"] == "stream":
+        assert p["n_chunk"] % 32 == 0
+        assert p["grid"] == -(-K // 128) * p["splits"]
     elif p["kernel"] == "tile":
         assert p["n_chunk"] % 64 == 0
         bm = 128 * p["rb"]

@@ -143,7 +143,8 @@ def test_grad_a_small_default_plan(lib, M, N, K):
 
 
 @pytest.mark.parametrize("kernel,rb,splits", [("tile", 1, 1), ("tile", 2, 1), ("tile", 1, 3), ("tile", 2, 2),
-                                              ("skinny", 0, 1), ("skinny", 0, 3)])
+                                              ("skinny", 0, 1), ("skinny", 0, 3),
+                                              ("stream", 0, 1), ("stream", 0, 3), ("stream", 0, 7)])
 @pytest.mark.parametrize("M,N,K", [(1, 300, 320), (5, 200, 192), (16, 1000, 512), (3, 129, 64), (12, 64, 1088)])
 def test_grad_a_every_variant_small(lib, kernel, rb, splits, M, N, K):
     g, s, b = random_inputs(M, N, K, seed=M + N * 3 + K * 5 + splits)
@@ -179,6 +180,25 @@ def test_grad_a_wide_deterministic_and_rejects_ragged_n(lib):
         assert np.array_equal(r1.view(np.uint32), r2.view(np.uint32))
     with pytest.raises(lib.Nf4Error):
         lib.grad_a_forced(dev(g[:, :4000]), sd[:4000], bd[:4000], "wide", rb=1)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (2, 33, 192), (7, 257, 320), (16, 2048, 640), (9, 5000, 128),
+                                   (16, 31, 64)])
+def test_grad_a_stream_ragged(lib, splits, M, N, K):
+    """Streaming kernel (M <= 16): N tails inside a k-step, chunk ends, K tails inside a strip."""
+    g, s, b = random_inputs(M, N, K, seed=13 * M + N + 3 * K + splits)
+    check_grad_a(lib, g, s, b, M, N, K, kernel="stream", splits=splits, what=f"stream s{splits} {M}x{N}x{K}")
+
+
+def test_grad_a_stream_deterministic(lib):
+    M, N, K = 16, 3000, 512
+    g, s, b = random_inputs(M, N, K, seed=77)
+    gd, sd, bd = dev(g), dev(s), dev(b)
+    for splits in (1, 4):
+        r1 = host(lib.grad_a_forced(gd, sd, bd, "stream", rb=0, splits=splits))
+        r2 = host(lib.grad_a_forced(gd, sd, bd, "stream", rb=0, splits=splits))
+        assert np.array_equal(r1.view(np.uint32), r2.view(np.uint32))
 
 
 PAGE_SHAPES = [(128, 1536, 1536), (64, 256, 128), (16, 64, 64), (512, 1536, 1536), (512, 256, 1536),
