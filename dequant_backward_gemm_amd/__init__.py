@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_PKG_DIR, "libnf4bwd.so")
 NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_HIP = 0, 1, 2, 3, 4
 
 EXPORTED_SYMBOLS = ("nf4_grad_a", "nf4_dequant", "nf4_pack", "nf4_status_string", "nf4_grad_a_plan",
-                    "nf4_grad_a_forced")
+                    "nf4_grad_a_forced", "nf4_release_workspaces")
 
 
 class Nf4Error(RuntimeError):
@@ -53,6 +53,8 @@ def _load() -> ctypes.CDLL:
     ci = ctypes.c_int
     lib.nf4_grad_a_forced.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, ci, vp]
     lib.nf4_grad_a_forced.restype = ctypes.c_int
+    lib.nf4_release_workspaces.argtypes = []
+    lib.nf4_release_workspaces.restype = ctypes.c_int
     return lib
 
 
@@ -70,6 +72,10 @@ def _ptr(t) -> int | None:
 def _stream_handle(stream) -> int | None:
     import torch
     if stream is None:
+        # the raw-handle query skips building a Stream object (a few us per call)
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return raw(torch.cuda.current_device())
         stream = torch.cuda.current_stream()
     return stream.cuda_stream
 
@@ -163,6 +169,11 @@ def pack(w, scales=None, codes=None, stream=None):
     _require(codes, torch.uint8, (N, K // 2), "codes")
     _check(pack_raw(_ptr(w), _ptr(scales), _ptr(codes), N, K, _stream_handle(stream)), "nf4_pack")
     return scales, codes
+
+
+def release_workspaces() -> None:
+    """Free the library's cached split-N workspaces (waits for the devices that hold one)."""
+    _check(_lib.nf4_release_workspaces(), "nf4_release_workspaces")
 
 
 def grad_a_plan(M: int, N: int, K: int) -> dict:

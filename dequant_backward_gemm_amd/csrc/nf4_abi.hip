@@ -76,13 +76,15 @@ int nf4_grad_a_plan(int64_t M, int64_t N, int64_t K, int* out5) {
   return NF4_OK;
 }
 
+int nf4_release_workspaces(void) { return from_hip(nf4::release_workspaces()); }
+
 const char* nf4_status_string(int status) {
   switch (status) {
     case NF4_OK: return "ok";
     case NF4_ERR_NULL: return "null pointer for a non-empty array";
     case NF4_ERR_SHAPE: return "bad shape (negative size, K not a multiple of 64, or size too large)";
     case NF4_ERR_ALIGN: return "pointer not 16-byte aligned";
-    case NF4_ERR_HIP: return "HIP launch or stream-ordered allocation failed";
+    case NF4_ERR_HIP: return "HIP launch, allocation or synchronisation failed";
     default: return "unknown nf4 status";
   }
 }

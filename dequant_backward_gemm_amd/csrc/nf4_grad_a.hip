@@ -605,10 +605,21 @@ __global__ __launch_bounds__(256) void grad_a_skinny_kernel(const float* __restr
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void grad_a_reduce_kernel(const floatx4* __restrict__ ws, floatx4* __restrict__ out,
                                                             int64_t n4, int splits) {
+  // out = ((ws_0 + ws_1) + ws_2) + ...; the partials are loaded eight at a
+  // time ahead of the adds, so a thread waits for one batch, not one load per
+  // split (the sum order is the same)
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
     floatx4 s = ws[i];
-    for (int p = 1; p < splits; ++p) s += ws[(int64_t)p * n4 + i];
+    for (int p = 1; p < splits; p += 8) {
+      floatx4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (p + u < splits) v[u] = ws[(int64_t)(p + u) * n4 + i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (p + u < splits) s += v[u];
+    }
     out[i] = s;
   }
 }

@@ -32,11 +32,12 @@ namespace nf4 {
 
 constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnyBK = 128;
-// Per-wave LDS in the loop: tables (4 groups of 8 rows x 2 blocks x 32 B, each
-// group padded by 64 B so that the groups a half-wave reads sit 64 B apart in
-// the bank space), then the grad_out staging slot.
-constexpr int kSkTabGroup = 8 * 2 * 32 + 64;          // 576
-constexpr int kSkTabBytes = 4 * kSkTabGroup;          // 2304
+// Per-wave LDS in the loop: tables, then the grad_out staging slot.  The
+// table of row 8q + e, block b sits at 256e + 64q + 32b: the 8 tables one
+// lookup instruction reads (fixed e) are one contiguous 256-byte run, the
+// layout measured closest to the LDS's per-instruction floor for random
+// 16-bit reads.
+constexpr int kSkTabBytes = 8 * 256;                  // 2048
 constexpr int kSkWaveBytes = kSkTabBytes + 1024;      // + A staging
 constexpr int kSkRedBytes = kSkinnyWaves * 16 * kSkinnyBK * 4;  // 64 KiB reduction buffer
 static_assert(kSkinnyWaves * kSkWaveBytes <= kSkRedBytes, "loop LDS fits in the reduction buffer");
@@ -71,11 +72,11 @@ __global__ __launch_bounds__(512, 2) void grad_a_stream_kernel(const float* __re
   const uint32_t wbase = (uint32_t)wave * kSkWaveBytes;
   // code dword of lane (ci, q): rows n0 + 8q + e, columns k0 + 8ci .. + 7
   const uint32_t cvoff = 8u * q * crow + (uint32_t)(k0 / 2 + 4 * ci);
-  // table reads of lane (ci, q): group q, block ci / 8, row e at +64e, code c at +2c
-  const uint32_t tlook = wbase + (uint32_t)q * kSkTabGroup + 32u * (uint32_t)(ci >> 3);
-  // table built by lane L: row L / 2 (group (L/2)/8, row (L/2)%8), block L % 2
+  // table reads of lane (ci, q): row e at +256e, group q, block ci / 8, code c at +2c
+  const uint32_t tlook = wbase + 64u * (uint32_t)q + 32u * (uint32_t)(ci >> 3);
+  // table built by lane L: row L / 2 (= 8q + e), block L % 2
   const int trow = lane >> 1, tkb = lane & 1;
-  const uint32_t tbuild = wbase + (uint32_t)(trow >> 3) * kSkTabGroup + 64u * (trow & 7) + 32u * tkb;
+  const uint32_t tbuild = wbase + 256u * (trow & 7) + 64u * (trow >> 3) + 32u * tkb;
   const uint32_t svoff = (uint32_t)trow * srow + 4u * (uint32_t)(k0 / 64 + tkb);
   // grad_out as loaded by lane L: row L / 4, values 8 * (L % 4) .. + 7 of the k-step;
   // staged at the A-operand slot of lane 16 * (L % 4) + L / 4
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(512, 2) void grad_a_stream_kernel(const float* __re
       constexpr int t = decltype(tc)::value;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        l[e] = lds_load_u16(smem, add_byte<(t >> 1)>(tlook, (t & 1) ? z[e] : y[e]) + 64u * e);
+        l[e] = lds_load_u16(smem, add_byte<(t >> 1)>(tlook, (t & 1) ? z[e] : y[e]) + 256u * e);
     };
     lookup(std::integral_constant<int, 0>{}, lk[0]);
     for_each_index(std::make_integer_sequence<int, 8>{}, [&](auto tc) {

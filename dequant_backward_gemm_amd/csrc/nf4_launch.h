@@ -34,6 +34,12 @@ GradAPlan plan_grad_a(int64_t M, int64_t N, int64_t K);
 // the combination is not valid for it.
 bool make_plan(int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, GradAPlan* out);
 
+// Split-N workspace of at least `bytes` for calls on `stream` (cached per
+// device and stream, grown with a stream-ordered allocation); and the release
+// of every cached workspace (drains the devices that hold one).
+hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** out);
+hipError_t release_workspaces();
+
 // Launch a given plan.
 hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const float* scales, const uint8_t* codes,
                               float* grad_a, int64_t M, int64_t N, int64_t K, hipStream_t stream);
@@ -48,7 +54,8 @@ hipError_t launch_grad_a_wide(int wc, int grid, const float* grad_out, const flo
                               hipStream_t stream);
 
 // Streaming kernel for M <= 16 (nf4_grad_a_skinny.hip): 128-column strips,
-// N-chunks of whole 32-row k-steps; needs 32-bit byte offsets.
+// N-chunks of whole 32-row k-steps, two 8-wave workgroups per CU; needs
+// 32-bit byte offsets.
 constexpr int kStreamBK = 128;
 bool stream_kernel_supported(int64_t M, int64_t N, int64_t K);
 hipError_t launch_grad_a_stream(int grid, const float* grad_out, const float* scales, const uint32_t* codes,

@@ -2,10 +2,80 @@
 // and split of N a shape gets, the split-N workspace and the fixed-order
 // reduction of the partials.
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "nf4_launch.h"
 
 namespace nf4 {
+
+// Split-N workspace: one buffer per (device, stream), grown on demand with a
+// stream-ordered allocation and kept for later calls on that stream.  Calls
+// on one stream run in order, so they can share it; calls on different
+// streams get different buffers.  (A stream-ordered allocate/free pair per
+// call cost more host time than a skinny call's kernels take.)
+namespace {
+struct Workspace {
+  int device;
+  hipStream_t stream;
+  void* ptr;
+  size_t bytes;
+};
+std::mutex g_ws_mutex;
+std::vector<Workspace> g_ws;
+}  // namespace
+
+hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const size_t want = (bytes + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);  // whole MiB
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace* w = nullptr;
+  for (auto& x : g_ws)
+    if (x.device == dev && x.stream == stream) w = &x;
+  if (w != nullptr && w->bytes >= bytes) {
+    *out = w->ptr;
+    return hipSuccess;
+  }
+  if (w == nullptr) {
+    g_ws.push_back(Workspace{dev, stream, nullptr, 0});
+    w = &g_ws.back();
+  }
+  if (w->ptr != nullptr) {
+    // the stream's earlier work still uses it: released in stream order
+    e = hipFreeAsync(w->ptr, stream);
+    w->ptr = nullptr;
+    w->bytes = 0;
+    if (e != hipSuccess) return e;
+  }
+  e = hipMallocAsync(&w->ptr, want, stream);
+  if (e != hipSuccess) {
+    w->ptr = nullptr;
+    return e;
+  }
+  w->bytes = want;
+  *out = w->ptr;
+  return hipSuccess;
+}
+
+hipError_t release_workspaces() {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int cur = 0;
+  hipError_t first = hipGetDevice(&cur);
+  for (auto& w : g_ws) {
+    if (w.ptr == nullptr) continue;
+    // every stream of the device drained first: the owning stream may be gone
+    hipError_t e = hipSetDevice(w.device);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipFreeAsync(w.ptr, nullptr);
+    if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+    if (e != hipSuccess && first == hipSuccess) first = e;
+  }
+  g_ws.clear();
+  hipError_t e = hipSetDevice(cur);
+  return first != hipSuccess ? first : e;
+}
 
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -22,28 +92,35 @@ GradAPlan plan_grad_a(int64_t M, int64_t N, int64_t K) {
   }
   const int64_t tiles_k = cdiv(K, 256);
   if (M <= 16 && stream_kernel_supported(M, N, K)) {
-    // Streaming kernel: 128-column strips x N-chunks.  Pick the chunk count by
-    // a bandwidth model: the weight stream runs at the chip rate once about
-    // two workgroups per CU are resident; a split adds its partials (written
-    // and read once) and the reduce launch.
+    // Streaming kernel: 128-column strips x N-chunks, two workgroups per CU.
+    // Pick the chunk count by a bandwidth model: the weight stream runs at
+    // the chip rate spread over the workgroup slots in use, in whole rounds
+    // of two workgroups per CU (a round started by a few leftover
+    // workgroups costs as much as a full one: measured 532 workgroups 30%
+    // slower than 504); a split adds its partials (written and read once)
+    // and the reduce launch.  Chunks shorter than one k-step per wave leave
+    // waves idle and are not considered.
     const int64_t tk = cdiv(K, kStreamBK);
     const double bw = 5.0e12;
     const double stream_bytes = (double)N * (double)K * (0.5 + 1.0 / 16.0) + 4.0 * (double)M * (double)(N + K);
+    const int64_t slots = 2 * kCUs;
     double best = 1e30;
     for (int64_t s = 1; s <= 64; ++s) {
       const int64_t chunk = cdiv(cdiv(N, s), 32) * 32;
       const int64_t se = cdiv(N, chunk);
-      if (se != s) continue;
-      const double occ = std::min(1.0, (double)(tk * se) / (2.0 * kCUs));
-      double t = stream_bytes / (bw * occ) + 3e-6;
-      if (se > 1) t += 2.0 * (double)se * (double)M * (double)K * 4.0 / bw + 6e-6;
+      if (se != s || (se > 1 && chunk < 256)) continue;
+      const int64_t grid = tk * se;
+      const double rounds = (double)cdiv(grid, slots);
+      // (each further round also pays a ramp of about 1.5 us)
+      double t = stream_bytes / bw * (rounds * slots) / (double)grid + 3e-6 + (rounds - 1.0) * 1.5e-6;
+      if (se > 1) t += 2.0 * (double)se * (double)M * (double)K * 4.0 / bw + 4e-6;
       if (t < best * 0.999) {
         best = t;
         p.kernel = 4;
         p.rb = 0;
         p.splits = (int)se;
         p.n_chunk = (int)chunk;
-        p.grid = (int)(tk * se);
+        p.grid = (int)grid;
       }
     }
     return p;
@@ -171,7 +248,7 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
   float* ws = nullptr;
   if (p.splits > 1) {
     const size_t bytes = (size_t)p.splits * (size_t)M * (size_t)K * sizeof(float);
-    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&ws), bytes, stream);
+    hipError_t e = stream_workspace(stream, bytes, reinterpret_cast<void**>(&ws));
     if (e != hipSuccess) return e;
     dst = ws;
   }
@@ -192,16 +269,11 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
     e = launch_grad_a_tile(p.rb, fast, p.grid, grad_out, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
                            (int)cdiv(M, 128 * p.rb), tiles_k, stream);
   }
-  if (e != hipSuccess) {
-    if (ws) (void)hipFreeAsync(ws, stream);
-    return e;
-  }
+  if (e != hipSuccess) return e;
   if (p.splits > 1) {
     const int64_t n4 = M * K / 4;
     const int grid = (int)std::min<int64_t>(cdiv(n4, 256), 8192);
     e = launch_grad_a_reduce(grid, ws, grad_a, n4, p.splits, stream);
-    hipError_t f = hipFreeAsync(ws, stream);
-    if (e == hipSuccess) e = f;
   }
   return e;
 }

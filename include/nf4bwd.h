@@ -35,8 +35,13 @@
  *     nothing has been enqueued.  NF4_ERR_HIP reports a failed launch or a
  *     failed stream-ordered allocation (hipGetLastError); the stream's later
  *     work is then undefined.
- *   - No state is kept across calls apart from a per-device property cache.
- *     Concurrent calls on different streams are safe.
+ *   - State kept across calls: the split-N workspace of nf4_grad_a, one
+ *     device buffer per (device, stream) that has needed one, grown on
+ *     demand and held until nf4_release_workspaces().  Calls on one stream
+ *     share it (they run in order); concurrent calls on different streams
+ *     use different buffers and are safe.  A stream handle that is destroyed
+ *     while its calls are still running must not be reused by a new stream
+ *     before they finish (the new stream would inherit the buffer).
  */
 #ifndef NF4BWD_H
 #define NF4BWD_H
@@ -53,7 +58,7 @@ typedef enum nf4_status {
   NF4_ERR_NULL = 1,   /* a required pointer is NULL while its array is non-empty */
   NF4_ERR_SHAPE = 2,  /* negative size, K % 64 != 0, or a size over 2^31-1 */
   NF4_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned */
-  NF4_ERR_HIP = 4     /* a HIP launch or stream-ordered allocation failed */
+  NF4_ERR_HIP = 4     /* a HIP launch, allocation or synchronisation failed */
 } nf4_status;
 
 /*
@@ -72,8 +77,9 @@ typedef enum nf4_status {
  *   Any M >= 0 and N >= 0 are accepted (tails are masked); N == 0 writes
  *   zeros; M == 0 or K == 0 enqueues nothing.  Results are bitwise
  *   deterministic for a given (M, N, K): no atomics, fixed summation order.
- *   Large N may use a stream-ordered device workspace (hipMallocAsync on
- *   `stream`, released on the same stream).
+ *   Large N may use the split-N workspace of `stream` (see the shared rules):
+ *   the first call that needs it, or a larger one, grows it with a
+ *   stream-ordered allocation (hipMallocAsync on `stream`).
  */
 int nf4_grad_a(const float* grad_out, const float* scales, const uint8_t* codes,
                float* grad_a, int64_t M, int64_t N, int64_t K, hipStream_t stream);
@@ -102,9 +108,10 @@ const char* nf4_status_string(int status);
 /*
  * nf4_grad_a_plan -- host-only introspection of the launch plan nf4_grad_a
  * uses for a shape (no device work).  out5 receives, in order: kernel
- * (0 = tiled, 1 = skinny M <= 16, 2 = zero fill for N == 0, 3 = wide tiled),
- * the kernel's tile parameter (tiled: 32-row blocks per wave; wide: column
- * groups of 128, the tile being 512 x 128 or 256 x 256), number of N-chunks
+ * (0 = tiled, 1 = skinny M <= 16, 2 = zero fill for N == 0, 3 = wide tiled,
+ * 4 = streaming M <= 16 with 128-column strips), the kernel's tile parameter
+ * (tiled: 32-row blocks per wave; wide: column groups of 128, the tile being
+ * 512 x 128 or 256 x 256; 0 for the others), number of N-chunks
  * (1 = no workspace), rows per N-chunk, workgroups of the main launch.
  * Returns NF4_ERR_SHAPE / NF4_ERR_NULL like nf4_grad_a.
  */
@@ -114,7 +121,9 @@ int nf4_grad_a_plan(int64_t M, int64_t N, int64_t K, int* out5);
  * nf4_grad_a_forced -- nf4_grad_a with the launch plan forced, for tests and
  * tuning: kernel 0 = tiled with `rb` (1 or 2) 32-row blocks per wave, kernel
  * 1 = skinny (requires M <= 16), kernel 3 = wide tiled with `rb` (1 or 2)
- * column groups (requires N % 64 == 0 and grad_out and the codes below 2 GiB);
+ * column groups (requires N % 64 == 0 and grad_out and the codes below 2 GiB),
+ * kernel 4 = streaming (requires M <= 16 and grad_out and the codes below
+ * 2 GiB; `rb` ignored);
  * `splits` = requested number of N-chunks
  * (rounded so that every chunk but the last is a whole number of stages).
  * Same contract and results-to-bound as nf4_grad_a; NF4_ERR_SHAPE if the
@@ -122,6 +131,15 @@ int nf4_grad_a_plan(int64_t M, int64_t N, int64_t K, int* out5);
  */
 int nf4_grad_a_forced(const float* grad_out, const float* scales, const uint8_t* codes, float* grad_a,
                       int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, hipStream_t stream);
+
+/*
+ * nf4_release_workspaces -- frees every cached split-N workspace.  It first
+ * waits for all work on each device that holds one (hipDeviceSynchronize),
+ * since the owning streams may no longer exist.  Host-blocking; not for use
+ * while another thread is calling nf4_grad_a.  Later calls allocate again as
+ * needed.  Returns NF4_OK or NF4_ERR_HIP.
+ */
+int nf4_release_workspaces(void);
 
 #ifdef __cplusplus
 }

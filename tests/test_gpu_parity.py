@@ -340,6 +340,29 @@ def test_grad_a_on_side_stream(lib):
     assert_within_bound(out.cpu().numpy(), ref, S, "side stream")
 
 
+def test_grad_a_split_workspace_per_stream(lib):
+    """Split plans on two streams at once, each stream's workspace growing from the smaller shape to the
+    larger, then the same after the cached workspaces are released."""
+    shapes = [(16, 3000, 512, 3), (8, 5000, 1024, 6)]  # (M, N, K, splits)
+    data = [random_inputs(M, N, K, seed=90 + i) for i, (M, N, K, _) in enumerate(shapes)]
+    refs = [oracle.grad_a(g, s, b, M, N, K) for (g, s, b), (M, N, K, _) in zip(data, shapes)]
+    devs = [(dev(g), dev(s), dev(b)) for g, s, b in data]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rnd in range(2):
+        torch.cuda.synchronize()
+        outs = []
+        for i, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                outs.append([lib.grad_a_forced(*devs[j], "stream", rb=0, splits=shapes[j][3]) for j in (i, 1 - i)])
+        for st in streams:
+            st.synchronize()
+        for i in range(2):
+            for k, j in enumerate((i, 1 - i)):
+                ref, S = refs[j]
+                assert_within_bound(outs[i][k].cpu().numpy(), ref, S, f"stream {i} shape {j} round {rnd}")
+        lib.release_workspaces()
+
+
 # --------------------------------------------------------------- edge cases
 
 def test_grad_a_empty_and_degenerate(lib):
