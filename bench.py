@@ -97,7 +97,12 @@ def kernel_name_for(plan, N=None):
     if plan["kernel"] == "zero_fill":
         return "fill_zero_kernel"
     if plan["kernel"] == "wide":
-        return "grad_a_wide_kernel<%d>" % plan["rb"]
+        return "grad_a_wide_kernel<%d, 0>" % plan["rb"]
+    if plan["kernel"] == "wide16":
+        # two kernels per call: the fp16 A-fragment pass, then the wide kernel reading the fragments
+        return "grad_out_frag_kernel+grad_a_wide_kernel<1, 3>"
+    if plan["kernel"] == "stream":
+        return "grad_a_stream_kernel<true>" if N is not None and N % 4 == 0 else "grad_a_stream_kernel<false>"
     if plan["rb"] == 2 and N is not None and N % 64 == 0:
         return "grad_a_tile_fast_kernel"
     return "grad_a_tile_kernel<%d>" % plan["rb"]
@@ -105,7 +110,8 @@ def kernel_name_for(plan, N=None):
 
 # Device code of the grad_A kernels; a recorded counter summary is valid only
 # for the sources it was taken on.
-KERNEL_SOURCES = ("nf4_grad_a.hip", "nf4_grad_a_wide.hip", "nf4_kernel_util.h", "nf4_device.h")
+KERNEL_SOURCES = ("nf4_grad_a.hip", "nf4_grad_a_wide.hip", "nf4_grad_a_skinny.hip", "nf4_kernel_util.h",
+                  "nf4_device.h")
 
 
 def source_digest():
@@ -218,22 +224,28 @@ def per_config_table(torch, nb):
     return out
 
 
-def cpu_baseline():
-    """The fp64 oracle, as it stands, on a bounded sample of one full-step layer."""
+def cpu_baseline(target_s=10.0, max_layers=8):
+    """The fp64 oracle, as it stands, on a bounded sample of the full step: one layer's seven projections at
+    3072 of the 8192 token rows each, repeated over further layers (fresh inputs) until about `target_s`
+    seconds of oracle time have accumulated, at most `max_layers` layers."""
     import numpy as np
     import oracle
     import synth
-    rows = 3072  # about 10-15 s of fp64 CPU work on the 16-core host share
+    rows = 3072
     flops = 0.0
     t = 0.0
-    for pi, (p, N, K) in enumerate(PROJ):
-        b = synth.random_code_bytes(N, K, seed=pi)
-        s = synth.random_scales_uniform(N, K, seed=pi + 10)
-        g = synth.grad_out_normal(rows, N, seed=pi + 20, std=1e-2)
-        t0 = time.perf_counter()
-        oracle.grad_a(g, s, b, rows, N, K, with_bound=False)
-        t += time.perf_counter() - t0
-        flops += 2.0 * rows * N * K
+    layers = 0
+    while layers < max_layers and (layers == 0 or t < target_s):
+        for pi, (p, N, K) in enumerate(PROJ):
+            seed = 100 * layers + pi
+            b = synth.random_code_bytes(N, K, seed=seed)
+            s = synth.random_scales_uniform(N, K, seed=seed + 10)
+            g = synth.grad_out_normal(rows, N, seed=seed + 20, std=1e-2)
+            t0 = time.perf_counter()
+            oracle.grad_a(g, s, b, rows, N, K, with_bound=False)
+            t += time.perf_counter() - t0
+            flops += 2.0 * rows * N * K
+        layers += 1
     try:
         cores = len(os.sched_getaffinity(0))
     except Exception:
@@ -241,8 +253,8 @@ def cpu_baseline():
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": min(cores, threads),
             "kind": "oracle", "seconds": round(t, 2),
-            "sample": f"one layer's 7 projections of the full step (q,k,v,o,gate,up,down) at {rows} of the 8192 "
-                      f"token rows each: numpy fp64 dequant + matmul, {flops / 1e9:.1f} GFLOP"}
+            "sample": f"{layers} layer(s) x the full step's 7 projections (q,k,v,o,gate,up,down) at {rows} of the "
+                      f"8192 token rows each: numpy fp64 dequant + matmul, {flops / 1e9:.1f} GFLOP"}
 
 
 def main():

@@ -45,11 +45,25 @@
 //   assigned so that a half-wave's fragment stores are consecutive dwords:
 //   no LDS access has bank conflicts.
 //
+// Fragment variant (AF): grad_out is first rounded to fp16 by a separate pass
+// (grad_out_frag_kernel) that writes it already in A-fragment order -- per
+// 16-row block and 32-row k-step, 64 lanes x 16 bytes, the same reduction
+// order as above -- so the main loop loads each A fragment with one 128-bit
+// load per lane (1 KiB contiguous per wave), with no rounding or exchange work
+// and half the bytes, and keeps AF k-steps of fragments in flight.
+//
 // Every global load is in bounds by clamping (rows of grad_out past M, code
-// columns past K, stages past the end of a chunk); such values only reach
-// outputs that are never stored or buffers that are never read.
+// columns past K, stages past the end of a chunk) or by the buffer range
+// (fragment rows past the padded M read zero); such values only reach outputs
+// that are never stored or buffers that are never read.
 #include "nf4_kernel_util.h"
 #include "nf4_launch.h"
+
+#include <algorithm>
+
+#ifndef WIDE_FRAG_DEPTH
+#define WIDE_FRAG_DEPTH 3
+#endif
 
 namespace nf4 {
 
@@ -80,10 +94,43 @@ __device__ __forceinline__ uint32_t table_pos(uint32_t slot) {
   return (slot & ~3u) | (((slot & 3u) + g) & 3u);
 }
 
-template <int WC>
+// grad_out -> fp16 A fragments.  Fragment (mb, ks) is 64 lanes x 16 bytes at
+// ((mb * N/32 + ks) * 64 + lane) * 16: lane (ci, q) holds rows 16mb + ci,
+// reduction rows 32ks + 16*(e/4) + 4q + e%4 for e = 0..7 (the order the wide
+// kernel's register transpose produces).  Rows past M are zero.
+__global__ __launch_bounds__(256) void grad_out_frag_kernel(const float* __restrict__ G, u32x4* __restrict__ F,
+                                                            int M, int N, int64_t total) {
+  const int ksn = N / 32;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x; f < total; f += stride) {
+    const int lane = (int)(f & 63);
+    const int64_t blk = f >> 6;
+    const int ks = (int)(blk % ksn);
+    const int64_t mb = blk / ksn;
+    const int64_t m = 16 * mb + (lane & 15);
+    const int n = 32 * ks + 4 * (lane >> 4);
+    u32x4 r = {0u, 0u, 0u, 0u};
+    if (m < M) {
+      const float* g = G + m * (int64_t)N + n;
+      const floatx4 a = *reinterpret_cast<const floatx4*>(g);
+      const floatx4 b = *reinterpret_cast<const floatx4*>(g + 16);
+      r[0] = pack_half2_rne(a[0], a[1]);
+      r[1] = pack_half2_rne(a[2], a[3]);
+      r[2] = pack_half2_rne(b[0], b[1]);
+      r[3] = pack_half2_rne(b[2], b[3]);
+    }
+    F[f] = r;
+  }
+}
+
+template <int WC, int AF>
 __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
-    const float* __restrict__ G, const float* __restrict__ S, const uint32_t* __restrict__ C32,
+    const void* __restrict__ Gv, const float* __restrict__ S, const uint32_t* __restrict__ C32,
     float* __restrict__ out, int M, int N, int K, int n_chunk, int tiles_m, int tiles_k) {
+  // AF == 0: Gv is grad_out (fp32 [M][N]); AF > 0: Gv holds the fp16 A
+  // fragments of grad_out_frag_kernel and AF k-steps of them are in flight.
+  static_assert(AF == 0 || AF == 1 || AF == 3, "fragment prefetch depth 1 or 3");
+  const float* __restrict__ G = static_cast<const float*>(Gv);
   using Cfg = WideCfg<WC>;
   constexpr int WR = Cfg::WR, BM = Cfg::BM, BK = Cfg::BK, KB = Cfg::KB;
   constexpr uint32_t kTabStage = Cfg::kTabStage, kFragStage = Cfg::kFragStage;
@@ -107,7 +154,9 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
 
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(C32, (uint32_t)((size_t)N * (size_t)K / 2));
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, (uint32_t)((size_t)N * (size_t)(K / 64) * 4));
-  const __amdgpu_buffer_rsrc_t rg = make_rsrc(G, (uint32_t)((size_t)M * (size_t)N * 4));
+  const int mpad = (M + 15) & ~15;
+  const __amdgpu_buffer_rsrc_t rg =
+      make_rsrc(G, (uint32_t)((size_t)(AF ? mpad : M) * (size_t)N * (AF ? 2 : 4)));
   const uint32_t crow = (uint32_t)K / 2;   // bytes per code row
   const uint32_t srow = (uint32_t)K / 16;  // bytes per scale row
   auto stage_row = [&](int st) { return (uint32_t)(nb + 64 * min(st, nst - 1)); };
@@ -122,6 +171,13 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
     voff_g[u] = (uint32_t)row * (uint32_t)N * 4u + 16u * (uint32_t)(lane & 3);
   }
   const uint32_t rbase = Cfg::kFragBase + (uint32_t)wc * 8192u + 16u * lane;
+  // fragment role (AF): fragment (mb, ks) of row block rb at
+  // ((mb * N/32 + ks) * 64 + lane) * 16, mb = (m0 + 64 wr) / 16 + rb; blocks
+  // past the padded M read zero through the buffer range
+  uint32_t voff_f[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+    voff_f[rb] = ((uint32_t)((m0 + 64 * wr) / 16 + rb) * (uint32_t)(N / 32) * 64u + (uint32_t)lane) * 16u;
 
   // ---- decode role: rows (nr0, nr0 + 1) of a stage, code dword 16*v + dl ----
   // Wave w takes the 8 stage rows that fill lane quarter q = w%4 of k-step
@@ -278,6 +334,15 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
       lds_store_u32(smem, wb + foff + (uint32_t)(v * 8192 + c * 1024), lk[v][0] | (lk[v][1] << 16));
   };
 
+  // fp16 A fragments of k-step j of the chunk (j = 2 * stage + s), 4 row blocks
+  auto load_af = [&](int j, u32x4 (&af)[4]) {
+    const uint32_t soff = (stage_row(j >> 1) / 32u + (uint32_t)(j & 1)) * 1024u;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) af[rb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, voff_f[rb], soff, 0));
+  };
+  constexpr int NAB = AF ? AF + 1 : 1;  // fragment buffers in the ring
+  u32x4 afr[NAB][4];
+
   float ar[8][4];       // grad_out of the next k-step, as loaded
   uint32_t xc[WC][2];   // codes of the stage decoded during the current one
   float sc[WC];         // scales of the tables built during the current stage
@@ -290,7 +355,12 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
     load_scales(1, s1);
     load_codes(0, x0);
     load_codes(1, xc);
-    load_a(0, 0, ar);
+    if constexpr (AF) {
+#pragma unroll
+      for (int j = 0; j < AF; ++j) load_af(j, afr[j]);
+    } else {
+      load_a(0, 0, ar);
+    }
     load_scales(2, sc);
     build_tables(s0, 0);
     build_tables(s1, kTabStage);
@@ -323,16 +393,26 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
     for_each_index(std::make_integer_sequence<int, 2>{}, [&](auto sc_) {
       constexpr int s = decltype(sc_)::value;
       constexpr int c0 = 4 * s;  // decode columns c0 .. c0 + 3 in this k-step
-      // round this k-step's grad_out (freeing the load registers), issue the
-      // next k-step's loads, then transpose: the loads do not wait for the
-      // transpose, and its temporaries never coexist with the raw values
-      uint32_t rr[8][2];
-      round_a(ar, rr);
-      __builtin_amdgcn_sched_barrier(0);
-      load_a(s == 0 ? st : st + 1, s ^ 1, ar);
-      __builtin_amdgcn_sched_barrier(0);
       u32x4 af[4];
-      to_a_frags(rr, af);
+      if constexpr (AF) {
+        // fragments of this k-step were loaded AF k-steps ago; issue the
+        // loads of k-step + AF into the buffer the previous k-step used
+        constexpr int b = (2 * (int)P + s) % NAB;
+        load_af(2 * st + s + AF, afr[(b + AF) % NAB]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) af[rb] = afr[b][rb];
+      } else {
+        // round this k-step's grad_out (freeing the load registers), issue the
+        // next k-step's loads, then transpose: the loads do not wait for the
+        // transpose, and its temporaries never coexist with the raw values
+        uint32_t rr[8][2];
+        round_a(ar, rr);
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(s == 0 ? st : st + 1, s ^ 1, ar);
+        __builtin_amdgcn_sched_barrier(0);
+        to_a_frags(rr, af);
+      }
       auto read_b = [&](int t) { return lds_load_u32x4(smem, rbase + frd + (uint32_t)((s * WC * 8 + t) * 1024)); };
       u32x4 bf[4];
       bf[0] = read_b(0);
@@ -403,11 +483,27 @@ hipError_t launch_grad_a_wide(int wc, int grid, const float* grad_out, const flo
                               float* dst, int M, int N, int K, int n_chunk, int tiles_m, int tiles_k,
                               hipStream_t stream) {
   if (wc == 2)
-    hipLaunchKernelGGL(grad_a_wide_kernel<2>, dim3(grid), dim3(512), 0, stream, grad_out, scales, codes, dst, M, N, K,
-                       n_chunk, tiles_m, tiles_k);
+    hipLaunchKernelGGL((grad_a_wide_kernel<2, 0>), dim3(grid), dim3(512), 0, stream, grad_out, scales, codes, dst, M,
+                       N, K, n_chunk, tiles_m, tiles_k);
   else
-    hipLaunchKernelGGL(grad_a_wide_kernel<1>, dim3(grid), dim3(512), 0, stream, grad_out, scales, codes, dst, M, N, K,
-                       n_chunk, tiles_m, tiles_k);
+    hipLaunchKernelGGL((grad_a_wide_kernel<1, 0>), dim3(grid), dim3(512), 0, stream, grad_out, scales, codes, dst, M,
+                       N, K, n_chunk, tiles_m, tiles_k);
+  return hipGetLastError();
+}
+
+size_t wide_frag_bytes(int64_t M, int64_t N) { return (size_t)((M + 15) / 16) * 16 * (size_t)N * 2; }
+
+hipError_t launch_grad_a_wide_frag(int grid, const float* grad_out, void* frags, const float* scales,
+                                   const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,
+                                   int tiles_k, hipStream_t stream) {
+  const int64_t total = (int64_t)((M + 15) / 16) * (N / 32) * 64;
+  const int pgrid = (int)std::min<int64_t>((total + 255) / 256, 16384);
+  hipLaunchKernelGGL(grad_out_frag_kernel, dim3(pgrid), dim3(256), 0, stream, grad_out, static_cast<u32x4*>(frags), M,
+                     N, total);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((grad_a_wide_kernel<1, WIDE_FRAG_DEPTH>), dim3(grid), dim3(512), 0, stream, frags, scales, codes,
+                     dst, M, N, K, n_chunk, tiles_m, tiles_k);
   return hipGetLastError();
 }
 

@@ -22,7 +22,8 @@ hipError_t launch_grad_a(const float* grad_out, const float* scales, const uint8
 // Launch plan chosen for a shape (exposed for tests and the benchmark).
 struct GradAPlan {
   int kernel;    // 0 = tile (BM = 128 * rb), 1 = skinny (M <= 16), 2 = zero-fill (N == 0),
-                 // 3 = wide (8 waves, tile (512 / rb) x (128 * rb)), 4 = stream (M <= 16)
+                 // 3 = wide (8 waves, tile (512 / rb) x (128 * rb)), 4 = stream (M <= 16),
+                 // 5 = wide fed by fp16 A fragments from a conversion pass (tile 512 x 128)
   int rb;        // tile: 32-row blocks per wave; wide: 128-column groups
   int splits;    // number of N-chunks (1 = no workspace, no reduce launch)
   int n_chunk;   // rows of N per chunk
@@ -52,6 +53,14 @@ int wide_tile_cols(int wc);
 hipError_t launch_grad_a_wide(int wc, int grid, const float* grad_out, const float* scales, const uint32_t* codes,
                               float* dst, int M, int N, int K, int n_chunk, int tiles_m, int tiles_k,
                               hipStream_t stream);
+
+// Fragment-fed wide kernel: grad_out converted once to fp16 A fragments in a
+// workspace of wide_frag_bytes(M, N) bytes, then the wide kernel (tile 512 x
+// 128) reads them.  Same preconditions as the wide kernel.
+size_t wide_frag_bytes(int64_t M, int64_t N);
+hipError_t launch_grad_a_wide_frag(int grid, const float* grad_out, void* frags, const float* scales,
+                                   const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,
+                                   int tiles_k, hipStream_t stream);
 
 // Streaming kernel for M <= 16 (nf4_grad_a_skinny.hip): 128-column strips,
 // N-chunks of whole 32-row k-steps, two 8-wave workgroups per CU; needs

@@ -147,14 +147,13 @@ GradAPlan plan_grad_a(int64_t M, int64_t N, int64_t K) {
   // partial-sum traffic of a split.
   const double cu_rate = 4096.0 * 2.4e9;  // fp16 MFMA flop/s per CU
   double best = 1e30;
-  // Splitting N pays only when the tiles alone leave most CUs idle: measured
-  // with the wide kernel, 48 tiles ran 9% faster split in two and 96 tiles 33%
-  // slower (partials, the reduce launch and cache pressure).  Problems under a
-  // GFLOP are launch-bound and never split.
+  // Splitting N pays only when the tiles alone leave CUs idle: measured with
+  // the fragment-fed wide kernel, 96 tiles ran 28% faster split in two and 48
+  // tiles 15%.  Problems under a GFLOP are launch-bound and never split.
   const bool tiny = 2.0 * (double)M * (double)N * (double)K < 1e9;
-  auto consider = [&](int kernel, int param, int64_t BM, int64_t BK, int per_cu, double eff) {
+  auto consider = [&](int kernel, int param, int64_t BM, int64_t BK, int per_cu, double eff, double fixed) {
     const int64_t tiles = cdiv(M, BM) * cdiv(K, BK);
-    const int64_t max_split = (tiny || tiles >= 64) ? 1 : cdiv(N, 64);
+    const int64_t max_split = (tiny || tiles >= kCUs) ? 1 : cdiv(N, 64);
     for (int64_t s = 1; s <= std::min<int64_t>(max_split, 16); ++s) {
       const int64_t chunk = cdiv(cdiv(N, s), 64) * 64;
       const int64_t se = cdiv(N, chunk);
@@ -162,10 +161,10 @@ GradAPlan plan_grad_a(int64_t M, int64_t N, int64_t K) {
       const int64_t units = tiles * se;
       const int64_t rounds = cdiv(units, (int64_t)kCUs * per_cu);
       const double t_unit = (double)BM * (double)BK * (double)chunk * 2.0 / (cu_rate * eff / per_cu);
-      double t = (double)rounds * t_unit + 3e-6;
-      // split partials: written once and read once by the reduce kernel (measured ~2.5 TB/s
-      // effective), plus the extra launch
-      if (se > 1) t += 2.0 * (double)se * (double)M * (double)K * 4.0 / 2.5e12 + 8e-6;
+      double t = (double)rounds * t_unit + 3e-6 + fixed;
+      // split partials: written once and read once by the reduce kernel (~5 TB/s), plus the
+      // reduce launch
+      if (se > 1) t += 2.0 * (double)se * (double)M * (double)K * 4.0 / 5.0e12 + 8e-6;
       if (t < best * 0.999) {
         best = t;
         p.kernel = kernel;
@@ -178,12 +177,15 @@ GradAPlan plan_grad_a(int64_t M, int64_t N, int64_t K) {
   };
   // measured on MI355X (fraction of the fp16 MFMA rate at M = 8192): tile
   // kernel with 128-row tiles (two workgroups per CU) ~0.24, 256-row tiles
-  // ~0.19; wide kernel 512 x 128 tiles ~0.28, 256 x 256 tiles ~0.11
-  consider(0, 2, 256, 256, 1, 0.19);
-  consider(0, 1, 128, 256, 2, 0.24);
+  // ~0.19; wide kernel 512 x 128 tiles ~0.28, 256 x 256 tiles ~0.11; wide
+  // kernel fed by fp16 A fragments ~0.40, plus its conversion pass (reads 4
+  // and writes 2 bytes per grad_out element, ~5.5 TB/s, and a launch)
+  consider(0, 2, 256, 256, 1, 0.19, 0.0);
+  consider(0, 1, 128, 256, 2, 0.24, 0.0);
   if (wide_kernel_supported(M, N, K)) {
-    consider(3, 1, wide_tile_rows(1), wide_tile_cols(1), 1, 0.28);
-    consider(3, 2, wide_tile_rows(2), wide_tile_cols(2), 1, 0.11);
+    consider(3, 1, wide_tile_rows(1), wide_tile_cols(1), 1, 0.28, 0.0);
+    consider(3, 2, wide_tile_rows(2), wide_tile_cols(2), 1, 0.11, 0.0);
+    consider(5, 1, wide_tile_rows(1), wide_tile_cols(1), 1, 0.40, 6.0 * (double)M * (double)N / 5.5e12 + 2e-6);
   }
   return p;
 }
@@ -220,6 +222,14 @@ bool make_plan(int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, 
     p.n_chunk = (int)chunk;
     p.splits = (int)cdiv(N, chunk);
     p.grid = (int)(cdiv(K, kStreamBK) * p.splits);
+  } else if (kernel == 5) {
+    if (!wide_kernel_supported(M, N, K)) return false;
+    const int64_t chunk = cdiv(cdiv(N, splits), 64) * 64;
+    p.kernel = 5;
+    p.rb = 1;
+    p.n_chunk = (int)chunk;
+    p.splits = (int)cdiv(N, chunk);
+    p.grid = (int)(cdiv(M, wide_tile_rows(1)) * cdiv(K, wide_tile_cols(1)) * p.splits);
   } else if (kernel == 3) {
     if ((rb != 1 && rb != 2) || !wide_kernel_supported(M, N, K)) return false;
     const int64_t chunk = cdiv(cdiv(N, splits), 64) * 64;
@@ -246,11 +256,20 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
   if (p.kernel == 2) return launch_fill_zero(p.grid, grad_a, M * K / 4, stream);
   float* dst = grad_a;
   float* ws = nullptr;
-  if (p.splits > 1) {
-    const size_t bytes = (size_t)p.splits * (size_t)M * (size_t)K * sizeof(float);
-    hipError_t e = stream_workspace(stream, bytes, reinterpret_cast<void**>(&ws));
-    if (e != hipSuccess) return e;
-    dst = ws;
+  void* frags = nullptr;
+  {
+    // workspace: split partials, then (fragment-fed wide kernel) the fp16 A fragments
+    const size_t part = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)K * sizeof(float) : 0;
+    const size_t part_al = (part + 255) & ~(size_t)255;
+    const size_t frag = p.kernel == 5 ? wide_frag_bytes(M, N) : 0;
+    if (part + frag > 0) {
+      char* base = nullptr;
+      hipError_t e = stream_workspace(stream, part_al + frag, reinterpret_cast<void**>(&base));
+      if (e != hipSuccess) return e;
+      if (part) ws = reinterpret_cast<float*>(base);
+      if (frag) frags = base + part_al;
+    }
+    if (ws) dst = ws;
   }
   const int tiles_k = (int)cdiv(K, 256);
   hipError_t e = hipSuccess;
@@ -259,6 +278,9 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
   } else if (p.kernel == 4) {
     e = launch_grad_a_stream(p.grid, grad_out, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
                              (int)cdiv(K, kStreamBK), stream);
+  } else if (p.kernel == 5) {
+    e = launch_grad_a_wide_frag(p.grid, grad_out, frags, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
+                                (int)cdiv(M, wide_tile_rows(1)), (int)cdiv(K, wide_tile_cols(1)), stream);
   } else if (p.kernel == 3) {
     e = launch_grad_a_wide(p.rb, p.grid, grad_out, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
                            (int)cdiv(M, wide_tile_rows(p.rb)), (int)cdiv(K, wide_tile_cols(p.rb)), stream);

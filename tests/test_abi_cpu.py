@@ -94,8 +94,8 @@ def test_plan_is_consistent(nb, M, N, K):
     if M <= 16:
         assert p["kernel"] in ("skinny", "stream")
     else:
-        assert p["kernel"] in ("tile", "wide")
-    if p["kernel"] == "wide":  # only where the wide kernel's preconditions hold
+        assert p["kernel"] in ("tile", "wide", "wide16")
+    if p["kernel"] in ("wide", "wide16"):  # only where the wide kernel's preconditions hold
         assert N % 64 == 0 and M * N * 4 < 2 ** 31 and N * K // 2 < 2 ** 31
     assert p["splits"] >= 1
     assert p["n_chunk"] * p["splits"] >= N > p["n_chunk"] * (p["splits"] - 1)
@@ -112,5 +112,6 @@ def test_plan_is_consistent(nb, M, N, K):
         assert p["grid"] == -(-M // bm) * tiles_k * p["splits"]
     else:
         assert p["n_chunk"] % 64 == 0 and p["rb"] in (1, 2)
+        assert p["kernel"] == "wide" or p["rb"] == 1
         bm, bk = 512 // p["rb"], 128 * p["rb"]
         assert p["grid"] == -(-M // bm) * -(-K // bk) * p["splits"]

@@ -170,6 +170,31 @@ def test_grad_a_wide_variants_ragged(lib, rb, splits, M, N, K):
                  what=f"wide rb{rb} s{splits} {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("M,N,K", [(17, 64, 64), (200, 384, 768), (513, 640, 320), (600, 1024, 448),
+                                   (1030, 256, 1088), (31, 128, 128)])
+def test_grad_a_wide16_variants_ragged(lib, splits, M, N, K):
+    """Wide kernel fed by the fp16 A-fragment pass: ragged M (fragment rows padded to 16, tile rows past
+    the padded M), ragged K, N splits sharing the workspace with the fragments."""
+    g, s, b = random_inputs(M, N, K, seed=M + 5 * N + K + 17 * splits)
+    check_grad_a(lib, g, s, b, M, N, K, kernel="wide16", rb=1, splits=splits,
+                 what=f"wide16 s{splits} {M}x{N}x{K}")
+
+
+def test_grad_a_wide16_matches_wide_bitwise(lib):
+    """Both grad_out paths give the same fp16 operands in the same reduction order, so the results are
+    bitwise equal."""
+    M, N, K = 700, 2048, 384
+    g, s, b = random_inputs(M, N, K, seed=37)
+    gd, sd, bd = dev(g), dev(s), dev(b)
+    for splits in (1, 2):
+        r1 = host(lib.grad_a_forced(gd, sd, bd, "wide", rb=1, splits=splits))
+        r2 = host(lib.grad_a_forced(gd, sd, bd, "wide16", rb=1, splits=splits))
+        assert np.array_equal(r1.view(np.uint32), r2.view(np.uint32))
+    with pytest.raises(lib.Nf4Error):
+        lib.grad_a_forced(dev(g[:, :2000]), sd[:2000], bd[:2000], "wide16", rb=1)
+
+
 def test_grad_a_wide_deterministic_and_rejects_ragged_n(lib):
     M, N, K = 700, 4096, 384
     g, s, b = random_inputs(M, N, K, seed=31)
