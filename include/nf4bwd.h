@@ -109,7 +109,8 @@ const char* nf4_status_string(int status);
  * nf4_grad_a_plan -- host-only introspection of the launch plan nf4_grad_a
  * uses for a shape (no device work).  out5 receives, in order: kernel
  * (0 = tiled, 1 = skinny M <= 16, 2 = zero fill for N == 0, 3 = wide tiled,
- * 4 = streaming M <= 16 with 128-column strips), the kernel's tile parameter
+ * 4 = streaming M <= 16 with 128-column strips, 5 = wide tiled fed by an fp16
+ * A-fragment conversion pass of grad_out), the kernel's tile parameter
  * (tiled: 32-row blocks per wave; wide: column groups of 128, the tile being
  * 512 x 128 or 256 x 256; 0 for the others), number of N-chunks
  * (1 = no workspace), rows per N-chunk, workgroups of the main launch.
@@ -123,7 +124,9 @@ int nf4_grad_a_plan(int64_t M, int64_t N, int64_t K, int* out5);
  * 1 = skinny (requires M <= 16), kernel 3 = wide tiled with `rb` (1 or 2)
  * column groups (requires N % 64 == 0 and grad_out and the codes below 2 GiB),
  * kernel 4 = streaming (requires M <= 16 and grad_out and the codes below
- * 2 GiB; `rb` ignored);
+ * 2 GiB; `rb` ignored), kernel 5 = wide tiled 512 x 128 fed by the fp16
+ * A-fragment pass (same requirements as kernel 3; `rb` ignored; the fragments
+ * take 2 * 16*ceil(M/16) * N bytes of the split-N workspace);
  * `splits` = requested number of N-chunks
  * (rounded so that every chunk but the last is a whole number of stages).
  * Same contract and results-to-bound as nf4_grad_a; NF4_ERR_SHAPE if the
