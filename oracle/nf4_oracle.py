@@ -24,7 +24,9 @@ fp32 then rounds it once: the oracle's dequant is bit-identical to the
 single fp32 multiply.
 
 grad_A is the definition itself: an fp64 matmul of grad_out and the fp32
-dequantised weights.  The companion ``S[m][k] = sum_n |g[m][n] * w[n][k]|``
+dequantised weights.  The forward product of the same layer (the page's header
+comment: C = A @ B over the shared dimension K) is likewise the definition,
+C = A . W^T in fp64.  The companion ``S[m][k] = sum_n |g[m][n] * w[n][k]|``
 is the scale the acceptance bound is stated against.
 
 Readings taken where the page is silent (each listed in the design notes):
@@ -134,6 +136,27 @@ def grad_a(grad_out: np.ndarray, scales: np.ndarray, code_bytes: np.ndarray, M: 
     if not with_bound:
         return ref
     return ref, np.abs(g) @ np.abs(w)
+
+
+def forward(a: np.ndarray, scales: np.ndarray, code_bytes: np.ndarray, M: int, N: int, K: int,
+            rows: np.ndarray | None = None, with_bound: bool = True):
+    """fp64 forward product of the same frozen layer and its bound scale S.
+
+    The subject page's header comment states the forward this backward kernel
+    is the analog of: C = A @ B with the shared dimension K, B_nf4 being
+    K x N.  With the stored W = B^T (N x K):
+
+        C[m][n] = sum_k a[m][k] * w[n][k];  S[m][n] = sum_k |a[m][k] * w[n][k]|.
+    """
+    w = dequant(scales, code_bytes, N, K).astype(np.float64)
+    x = np.asarray(a, dtype=np.float32).reshape(M, K)
+    if rows is not None:
+        x = x[np.asarray(rows)]
+    x = x.astype(np.float64)
+    ref = x @ w.T
+    if not with_bound:
+        return ref
+    return ref, np.abs(x) @ np.abs(w).T
 
 
 def grad_a_fp16_operands(grad_out: np.ndarray, scales: np.ndarray, code_bytes: np.ndarray,

@@ -198,6 +198,77 @@ def test_grad_a_special_cases():
     assert np.allclose(ref, alt, rtol=1e-12, atol=1e-12)
 
 
+# ----------------------------------------------------------------- forward C = A . W^T
+
+@pytest.mark.parametrize("M,N,K,seed", [(1, 1, 64, 0), (3, 5, 64, 1), (4, 17, 128, 2), (2, 9, 192, 3)])
+def test_forward_matches_fsum_bruteforce(M, N, K, seed):
+    b = synth.random_code_bytes(N, K, seed + 50)
+    s = synth.random_scales_uniform(N, K, seed + 150)
+    a = synth.grad_out_normal(M, K, seed + 250)
+    ref, S = oracle.forward(a, s, b, M, N, K)
+    w = oracle.dequant(s, b, N, K).astype(np.float64)
+    ad = a.astype(np.float64)
+    for m in range(M):
+        for n in range(N):
+            exact = math.fsum(float(ad[m, k]) * float(w[n, k]) for k in range(K))
+            bound = math.fsum(abs(float(ad[m, k]) * float(w[n, k])) for k in range(K))
+            assert abs(ref[m, n] - exact) <= 1e-12 * bound + 1e-300
+            assert abs(S[m, n] - bound) <= 1e-13 * bound
+
+
+def test_forward_one_hot_rows_pick_weight_columns():
+    """A row of A that is e_k0 gives the dequantised column k0 of W (every out-feature's weight at k0)."""
+    M, N, K = 5, 11, 192
+    b = synth.random_code_bytes(N, K, seed=61)
+    s = synth.random_scales_uniform(N, K, seed=62)
+    a = np.zeros((M, K), dtype=np.float32)
+    picks = [0, 63, 64, 191, 100]
+    for m, k in enumerate(picks):
+        a[m, k] = 1.0
+    ref, _ = oracle.forward(a, s, b, M, N, K)
+    w = oracle.dequant(s, b, N, K)
+    for m, k in enumerate(picks):
+        assert np.array_equal(ref[m], w[:, k].astype(np.float64))
+
+
+def test_forward_is_the_adjoint_of_grad_a():
+    """<forward(A), X> = <A, grad_a(X)>: the two oracles contract the same weights over different
+    dimensions, so a transposed operand or a swapped dimension in either breaks this."""
+    M, N, K = 6, 40, 256
+    b = synth.random_code_bytes(N, K, seed=71)
+    s = synth.random_scales_uniform(N, K, seed=72)
+    a = synth.grad_out_normal(M, K, seed=73)
+    x = synth.grad_out_normal(M, N, seed=74)
+    c, _ = oracle.forward(a, s, b, M, N, K)
+    ga, _ = oracle.grad_a(x, s, b, M, N, K)
+    lhs = np.sum(c * x.astype(np.float64))
+    rhs = np.sum(a.astype(np.float64) * ga)
+    assert abs(lhs - rhs) <= 1e-11 * (np.sum(np.abs(c * x)) + 1.0)
+
+
+def test_forward_special_cases():
+    M, N, K = 4, 24, 128
+    a = synth.grad_out_normal(M, K, seed=81)
+    # all codes 7 -> zero output
+    b7 = np.full((N, K // 2), 0x77, dtype=np.uint8)
+    s = synth.random_scales_uniform(N, K, seed=82)
+    ref, _ = oracle.forward(a, s, b7, M, N, K)
+    assert np.all(ref == 0.0)
+    # unit scales and all codes 15 -> every output column is the row sum of A
+    bF = np.full((N, K // 2), 0xFF, dtype=np.uint8)
+    ref, _ = oracle.forward(a, np.ones((N, K // 64), dtype=np.float32), bF, M, N, K)
+    rs = np.sum(a.astype(np.float64), axis=1)
+    assert np.allclose(ref, np.repeat(rs[:, None], N, axis=1), rtol=1e-14, atol=1e-14)
+    # one nonzero weight at (n0, k0) with scale 0.5: column n0 of C is 0.5 * column k0 of A
+    n0, k0 = 7, 45
+    b = np.full((N, K // 2), 0x77, dtype=np.uint8)
+    b[n0, k0 // 2] = (0x7 | (15 << 4)) if k0 % 2 else (0x70 | 15)
+    ref, _ = oracle.forward(a, np.full((N, K // 64), 0.5, dtype=np.float32), b, M, N, K)
+    want = np.zeros((M, N))
+    want[:, n0] = 0.5 * a[:, k0].astype(np.float64)
+    assert np.array_equal(ref, want)
+
+
 def test_fp16_operand_reference_rounds_to_nearest_even():
     """The diagnostic reference converts with RNE (ties to even), not toward zero."""
     one = np.float32(1.0)
