@@ -100,7 +100,7 @@ def kernel_name_for(plan, N=None):
         return "grad_a_wide_kernel<%d, 0>" % plan["rb"]
     if plan["kernel"] == "wide16":
         # two kernels per call: the fp16 A-fragment pass, then the wide kernel reading the fragments
-        return "grad_out_frag_kernel+grad_a_wide_kernel<1, 3>"
+        return "grad_out_frag_kernel<false>+grad_a_wide_kernel<1, 3>"
     if plan["kernel"] == "stream":
         return "grad_a_stream_kernel<true>" if N is not None and N % 4 == 0 else "grad_a_stream_kernel<false>"
     if plan["rb"] == 2 and N is not None and N % 64 == 0:
@@ -157,8 +157,9 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "copies": 3}), flush=True)
 
 
-def time_config(torch, nb, M, N, K, seed, g_std, rotate_bytes=512 << 20, target_s=0.02, trials=5):
-    """Median per-call time of nf4_grad_a over rotated input sets (each set: codes, scales, grad_out)."""
+def time_config(torch, nb, M, N, K, seed, g_std, rotate_bytes=512 << 20, target_s=0.02, trials=5, op="grad_a"):
+    """Median per-call time of nf4_grad_a (or, op="forward", nf4_forward) over rotated input sets (each set:
+    codes, scales, grad_out [M][N] or activations [M][K])."""
     per_set = alg_bytes(M, N, K)
     nsets = max(2, -(-rotate_bytes // per_set))
     nsets = min(nsets, 64)
@@ -169,16 +170,21 @@ def time_config(torch, nb, M, N, K, seed, g_std, rotate_bytes=512 << 20, target_
         w = torch.empty((N, K), device="cuda").normal_(0.0, 0.02, generator=gen)
         s, c = nb.pack(w)
         del w
-        g = torch.empty((M, N), device="cuda").normal_(0.0, g_std, generator=gen)
-        o = torch.empty((M, K), device="cuda")
+        if op == "forward":
+            g = torch.empty((M, K), device="cuda").normal_(0.0, g_std, generator=gen)
+            o = torch.empty((M, N), device="cuda")
+        else:
+            g = torch.empty((M, N), device="cuda").normal_(0.0, g_std, generator=gen)
+            o = torch.empty((M, K), device="cuda")
         sets.append((g, s, c, o))
+    call = nb.forward if op == "forward" else nb.grad_a
     torch.cuda.synchronize()
     for i in range(5):
         g, s, c, o = sets[i % nsets]
-        nb.grad_a(g, s, c, out=o)
+        call(g, s, c, out=o)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    nb.grad_a(*sets[0][:3], out=sets[0][3])
+    call(*sets[0][:3], out=sets[0][3])
     torch.cuda.synchronize()
     one = max(time.perf_counter() - t0, 1e-6)
     reps = int(min(max(target_s / one, 2 * nsets), 20000))
@@ -189,7 +195,7 @@ def time_config(torch, nb, M, N, K, seed, g_std, rotate_bytes=512 << 20, target_
         e0.record()
         for r in range(reps):
             g, s, c, o = sets[r % nsets]
-            nb.grad_a(g, s, c, out=o)
+            call(g, s, c, out=o)
         e1.record()
         torch.cuda.synchronize()
         res.append(e0.elapsed_time(e1) * 1e-3 / reps)
@@ -199,14 +205,20 @@ def time_config(torch, nb, M, N, K, seed, g_std, rotate_bytes=512 << 20, target_
     return res[len(res) // 2], res[0], res[-1], nsets
 
 
-def per_config_table(torch, nb):
+def per_config_table(torch, nb, op="grad_a"):
+    """Per-configuration timing of nf4_grad_a, or (op="forward") of the same layers' forward product
+    nf4_forward (activations [M][K] with the configuration's grad_out distribution, output [M][N];
+    the full-step layer shapes are added for the forward)."""
     import synth
     out = {}
     plan = [("tiny", synth.CONFIGS["tiny"], 1.0), ("attn_proj", synth.CONFIGS["attn_proj"], 1e-2),
             ("mlp_pair", synth.CONFIGS["mlp_pair"], 1e-2), ("skinny", synth.SKINNY_SHAPES, 1.0)]
+    if op == "forward":
+        full = [synth.Shape(f"full_step_{p}", M_STEP, N, K) for (p, N, K) in PROJ if p in ("q", "k", "gate", "down")]
+        plan.append(("full_step", full, 1e-2))
     for cname, shapes, gstd in plan:
         for i, shp in enumerate(shapes):
-            med, lo, hi, nsets = time_config(torch, nb, shp.M, shp.N, shp.K, seed=i, g_std=gstd)
+            med, lo, hi, nsets = time_config(torch, nb, shp.M, shp.N, shp.K, seed=i, g_std=gstd, op=op)
             fl = 2.0 * shp.M * shp.N * shp.K
             by = alg_bytes(shp.M, shp.N, shp.K)
             tf = fl / med / 1e12
@@ -218,16 +230,19 @@ def per_config_table(torch, nb):
                 "tflops": round(tf, 2), "gbs": round(gb, 1), "bound": bound,
                 "frac_of_bound": round(tf / PEAK_FP16_TFLOPS if bound == "mfma" else gb / PEAK_HBM_GBS, 4),
                 "frac_of_roofline_time": round(roofline_time(shp.M, shp.N, shp.K) / med, 4),
-                "rotated_input_sets": nsets, "plan": nb.grad_a_plan(shp.M, shp.N, shp.K),
+                "rotated_input_sets": nsets,
             }
-            log(f"[bench] {shp.name}: {med * 1e6:.1f} us  {tf:.1f} TFLOP/s  {gb:.0f} GB/s")
+            if op == "grad_a":
+                out[shp.name]["plan"] = nb.grad_a_plan(shp.M, shp.N, shp.K)
+            log(f"[bench] {op} {shp.name}: {med * 1e6:.1f} us  {tf:.1f} TFLOP/s  {gb:.0f} GB/s")
     return out
 
 
-def cpu_baseline(target_s=10.0, max_layers=8):
+def cpu_baseline(target_s=10.0, max_layers=8, op="grad_a"):
     """The fp64 oracle, as it stands, on a bounded sample of the full step: one layer's seven projections at
     3072 of the 8192 token rows each, repeated over further layers (fresh inputs) until about `target_s`
-    seconds of oracle time have accumulated, at most `max_layers` layers."""
+    seconds of oracle time have accumulated, at most `max_layers` layers.  op="forward" times the forward
+    oracle on the same layers (activations [rows][K])."""
     import numpy as np
     import oracle
     import synth
@@ -240,9 +255,14 @@ def cpu_baseline(target_s=10.0, max_layers=8):
             seed = 100 * layers + pi
             b = synth.random_code_bytes(N, K, seed=seed)
             s = synth.random_scales_uniform(N, K, seed=seed + 10)
-            g = synth.grad_out_normal(rows, N, seed=seed + 20, std=1e-2)
-            t0 = time.perf_counter()
-            oracle.grad_a(g, s, b, rows, N, K, with_bound=False)
+            if op == "forward":
+                a = synth.grad_out_normal(rows, K, seed=seed + 20, std=1e-2)
+                t0 = time.perf_counter()
+                oracle.forward(a, s, b, rows, N, K, with_bound=False)
+            else:
+                g = synth.grad_out_normal(rows, N, seed=seed + 20, std=1e-2)
+                t0 = time.perf_counter()
+                oracle.grad_a(g, s, b, rows, N, K, with_bound=False)
             t += time.perf_counter() - t0
             flops += 2.0 * rows * N * K
         layers += 1
@@ -253,8 +273,8 @@ def cpu_baseline(target_s=10.0, max_layers=8):
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": min(cores, threads),
             "kind": "oracle", "seconds": round(t, 2),
-            "sample": f"{layers} layer(s) x the full step's 7 projections (q,k,v,o,gate,up,down) at {rows} of the "
-                      f"8192 token rows each: numpy fp64 dequant + matmul, {flops / 1e9:.1f} GFLOP"}
+            "sample": f"{op}: {layers} layer(s) x the full step's 7 projections (q,k,v,o,gate,up,down) at {rows} "
+                      f"of the 8192 token rows each: numpy fp64 dequant + matmul, {flops / 1e9:.1f} GFLOP"}
 
 
 def main():
@@ -264,6 +284,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config table")
+    ap.add_argument("--forward-configs", action="store_true",
+                    help="only the forward product's per-config table and its CPU oracle baseline (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for scaling HBM byte counters) and exit")
     args = ap.parse_args()
@@ -277,6 +299,12 @@ def main():
         copy_calibration(torch)
         return
     import dequant_backward_gemm_amd as nb
+
+    if args.forward_configs:
+        rec = {"per_config_forward": per_config_table(torch, nb, op="forward"),
+               "cpu_baseline_forward": None if args.no_cpu else cpu_baseline(target_s=5.0, op="forward")}
+        print(json.dumps(rec), flush=True)
+        return
 
     props = torch.cuda.get_device_properties(0)
     log(f"[bench] device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
@@ -333,6 +361,7 @@ def main():
             "kernel_source_digest": source_digest()}
 
     per_config = None if args.no_configs else per_config_table(torch, nb)
+    per_config_fwd = None if args.no_configs else per_config_table(torch, nb, op="forward")
     cpu = None if args.no_cpu else cpu_baseline()
 
     rec = {
@@ -361,6 +390,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_config": per_config,
+        "per_config_forward": per_config_fwd,
     }
     print(json.dumps(rec), flush=True)
 

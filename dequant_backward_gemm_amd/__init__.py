@@ -6,6 +6,7 @@ stream.  Importing this module loads the in-tree library and fails loudly if
 it is missing; there is no fallback of any kind.
 
     grad_a(grad_out, scales, codes)  -> fp32 [M, K]
+    forward(a, scales, codes)        -> fp32 [M, N]   (the same layer's forward product)
     dequant(scales, codes, N, K)     -> fp32 [N, K]
     pack(w)                          -> (scales fp32 [N, K/64], codes uint8 [N, K/2])
 
@@ -24,7 +25,7 @@ LIB_PATH = os.path.join(_PKG_DIR, "libnf4bwd.so")
 NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_HIP = 0, 1, 2, 3, 4
 
 EXPORTED_SYMBOLS = ("nf4_grad_a", "nf4_dequant", "nf4_pack", "nf4_status_string", "nf4_grad_a_plan",
-                    "nf4_grad_a_forced", "nf4_release_workspaces")
+                    "nf4_grad_a_forced", "nf4_release_workspaces", "nf4_forward", "nf4_forward_forced")
 
 
 class Nf4Error(RuntimeError):
@@ -53,6 +54,10 @@ def _load() -> ctypes.CDLL:
     ci = ctypes.c_int
     lib.nf4_grad_a_forced.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, ci, vp]
     lib.nf4_grad_a_forced.restype = ctypes.c_int
+    lib.nf4_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.nf4_forward.restype = ctypes.c_int
+    lib.nf4_forward_forced.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp]
+    lib.nf4_forward_forced.restype = ctypes.c_int
     lib.nf4_release_workspaces.argtypes = []
     lib.nf4_release_workspaces.restype = ctypes.c_int
     return lib
@@ -140,6 +145,26 @@ def grad_a_forced(grad_out, scales, codes, kernel: str, rb: int = 2, splits: int
     kid = {"tile": 0, "skinny": 1, "wide": 3, "stream": 4, "wide16": 5}[kernel]
     _check(_lib.nf4_grad_a_forced(_ptr(grad_out), _ptr(scales), _ptr(codes), _ptr(out), M, N, K, kid, rb, splits,
                                   _stream_handle(stream)), "nf4_grad_a_forced")
+    return out
+
+
+def forward(a, scales, codes, out=None, stream=None, splits: int = 0):
+    """c[M, N] = a[M, K] . dequant(codes, scales)[N, K]^T (fp32); splits > 0 forces the K chunk count."""
+    import torch
+    M, K = a.shape
+    N = codes.shape[0]
+    _require(a, torch.float32, (M, K), "a")
+    _require(scales, torch.float32, (N, K // 64), "scales")
+    _require(codes, torch.uint8, (N, K // 2), "codes")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    _require(out, torch.float32, (M, N), "out")
+    if splits > 0:
+        st = _lib.nf4_forward_forced(_ptr(a), _ptr(scales), _ptr(codes), _ptr(out), M, N, K, splits,
+                                     _stream_handle(stream))
+    else:
+        st = _lib.nf4_forward(_ptr(a), _ptr(scales), _ptr(codes), _ptr(out), M, N, K, _stream_handle(stream))
+    _check(st, "nf4_forward")
     return out
 
 

@@ -94,10 +94,13 @@ __device__ __forceinline__ uint32_t table_pos(uint32_t slot) {
   return (slot & ~3u) | (((slot & 3u) + g) & 3u);
 }
 
-// grad_out -> fp16 A fragments.  Fragment (mb, ks) is 64 lanes x 16 bytes at
-// ((mb * N/32 + ks) * 64 + lane) * 16: lane (ci, q) holds rows 16mb + ci,
+// fp32 [M][N] -> fp16 MFMA A fragments (the A operand of a product whose
+// reduction runs along N).  Fragment (mb, ks) is 64 lanes x 16 bytes at
+// ((mb * N/32 + ks) * 64 + lane) * 16: lane (ci, q) holds row 16mb + ci at
 // reduction rows 32ks + 16*(e/4) + 4q + e%4 for e = 0..7 (the order the wide
-// kernel's register transpose produces).  Rows past M are zero.
+// kernel's register transpose produces) or, NATURAL, 32ks + 8q + e.  Rows
+// past M are zero.
+template <bool NATURAL>
 __global__ __launch_bounds__(256) void grad_out_frag_kernel(const float* __restrict__ G, u32x4* __restrict__ F,
                                                             int M, int N, int64_t total) {
   const int ksn = N / 32;
@@ -108,12 +111,12 @@ __global__ __launch_bounds__(256) void grad_out_frag_kernel(const float* __restr
     const int ks = (int)(blk % ksn);
     const int64_t mb = blk / ksn;
     const int64_t m = 16 * mb + (lane & 15);
-    const int n = 32 * ks + 4 * (lane >> 4);
+    const int n = 32 * ks + (NATURAL ? 8 : 4) * (lane >> 4);
     u32x4 r = {0u, 0u, 0u, 0u};
     if (m < M) {
       const float* g = G + m * (int64_t)N + n;
       const floatx4 a = *reinterpret_cast<const floatx4*>(g);
-      const floatx4 b = *reinterpret_cast<const floatx4*>(g + 16);
+      const floatx4 b = *reinterpret_cast<const floatx4*>(g + (NATURAL ? 4 : 16));
       r[0] = pack_half2_rne(a[0], a[1]);
       r[1] = pack_half2_rne(a[2], a[3]);
       r[2] = pack_half2_rne(b[0], b[1]);
@@ -493,14 +496,22 @@ hipError_t launch_grad_a_wide(int wc, int grid, const float* grad_out, const flo
 
 size_t wide_frag_bytes(int64_t M, int64_t N) { return (size_t)((M + 15) / 16) * 16 * (size_t)N * 2; }
 
+hipError_t launch_frag_pass(const float* src, void* frags, int rows, int cols, bool natural, hipStream_t stream) {
+  const int64_t total = (int64_t)((rows + 15) / 16) * (cols / 32) * 64;
+  const int pgrid = (int)std::min<int64_t>((total + 255) / 256, 16384);
+  if (natural)
+    hipLaunchKernelGGL(grad_out_frag_kernel<true>, dim3(pgrid), dim3(256), 0, stream, src, static_cast<u32x4*>(frags),
+                       rows, cols, total);
+  else
+    hipLaunchKernelGGL(grad_out_frag_kernel<false>, dim3(pgrid), dim3(256), 0, stream, src, static_cast<u32x4*>(frags),
+                       rows, cols, total);
+  return hipGetLastError();
+}
+
 hipError_t launch_grad_a_wide_frag(int grid, const float* grad_out, void* frags, const float* scales,
                                    const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,
                                    int tiles_k, hipStream_t stream) {
-  const int64_t total = (int64_t)((M + 15) / 16) * (N / 32) * 64;
-  const int pgrid = (int)std::min<int64_t>((total + 255) / 256, 16384);
-  hipLaunchKernelGGL(grad_out_frag_kernel, dim3(pgrid), dim3(256), 0, stream, grad_out, static_cast<u32x4*>(frags), M,
-                     N, total);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_frag_pass(grad_out, frags, M, N, /*natural=*/false, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((grad_a_wide_kernel<1, WIDE_FRAG_DEPTH>), dim3(grid), dim3(512), 0, stream, frags, scales, codes,
                      dst, M, N, K, n_chunk, tiles_m, tiles_k);

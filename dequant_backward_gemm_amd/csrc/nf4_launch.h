@@ -62,6 +62,21 @@ hipError_t launch_grad_a_wide_frag(int grid, const float* grad_out, void* frags,
                                    const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,
                                    int tiles_k, hipStream_t stream);
 
+// fp32 [rows][cols] -> fp16 MFMA A fragments (reduction along cols, cols % 32
+// == 0), rows padded to 16 with zeros: the backward wide kernel's permuted
+// reduction order, or natural order for the forward kernel.
+hipError_t launch_frag_pass(const float* src, void* frags, int rows, int cols, bool natural, hipStream_t stream);
+
+// Forward product C[M][N] = A[M][K] . dequant(W)^T (nf4_forward.hip): 512 x 128
+// tiles, K split into chunks of whole 64-wide stages; A converted first into
+// fragments (forward_frag_bytes(M, K) bytes of workspace).
+bool forward_supported(int64_t M, int64_t N, int64_t K);
+size_t forward_frag_bytes(int64_t M, int64_t K);
+hipError_t launch_forward(int grid, const float* a, void* frags, const float* scales, const uint32_t* codes,
+                          float* dst, int M, int N, int K, int k_chunk, int tiles_m, int tiles_n, hipStream_t stream);
+hipError_t launch_nf4_forward(const float* a, const float* scales, const uint8_t* codes, float* c, int64_t M,
+                              int64_t N, int64_t K, int splits, hipStream_t stream);
+
 // Streaming kernel for M <= 16 (nf4_grad_a_skinny.hip): 128-column strips,
 // N-chunks of whole 32-row k-steps, two 8-wave workgroups per CU; needs
 // 32-bit byte offsets.

@@ -300,4 +300,50 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
   return e;
 }
 
+// Forward product: 512 x 128 tiles over (M, N); when they leave CUs idle the K
+// reduction is split into chunks of whole 64-wide stages (fp32 partials in the
+// stream's workspace, summed in chunk order by the reduce kernel).  splits <= 0
+// picks the count by the same cost model as the backward tiles.
+hipError_t launch_nf4_forward(const float* a, const float* scales, const uint8_t* codes, float* c, int64_t M,
+                              int64_t N, int64_t K, int splits, hipStream_t stream) {
+  if (K == 0) return launch_fill_zero((int)std::min<int64_t>(cdiv(M * N / 4, 256), 4096), c, M * N / 4, stream);
+  const int64_t tiles_m = cdiv(M, 512), tiles_n = cdiv(N, 128);
+  const int64_t tiles = tiles_m * tiles_n;
+  int64_t se = 1, chunk = K;
+  if (splits > 0) {
+    chunk = cdiv(cdiv(K, splits), 64) * 64;
+    se = cdiv(K, chunk);
+  } else if (tiles < kCUs) {
+    const double cu_rate = 4096.0 * 2.4e9 * 0.40;  // fp16 MFMA flop/s per CU at the measured efficiency
+    double best = 1e30;
+    for (int64_t s = 1; s <= 16; ++s) {
+      const int64_t ch = cdiv(cdiv(K, s), 64) * 64;
+      const int64_t e = cdiv(K, ch);
+      if (e != s) continue;
+      const int64_t rounds = cdiv(tiles * e, kCUs);
+      double t = (double)rounds * (512.0 * 128.0 * (double)ch * 2.0 / cu_rate);
+      if (e > 1) t += 2.0 * (double)e * (double)M * (double)N * 4.0 / 5.0e12 + 8e-6;
+      if (t < best * 0.999) {
+        best = t;
+        se = e;
+        chunk = ch;
+      }
+    }
+  }
+  const size_t part = se > 1 ? (size_t)se * (size_t)M * (size_t)N * sizeof(float) : 0;
+  const size_t part_al = (part + 255) & ~(size_t)255;
+  char* base = nullptr;
+  hipError_t e = stream_workspace(stream, part_al + forward_frag_bytes(M, K), reinterpret_cast<void**>(&base));
+  if (e != hipSuccess) return e;
+  float* dst = se > 1 ? reinterpret_cast<float*>(base) : c;
+  e = launch_forward((int)(tiles * se), a, base + part_al, scales, reinterpret_cast<const uint32_t*>(codes), dst,
+                     (int)M, (int)N, (int)K, (int)chunk, (int)tiles_m, (int)tiles_n, stream);
+  if (e != hipSuccess) return e;
+  if (se > 1) {
+    const int64_t n4 = M * N / 4;
+    e = launch_grad_a_reduce((int)std::min<int64_t>(cdiv(n4, 256), 8192), dst, c, n4, (int)se, stream);
+  }
+  return e;
+}
+
 }  // namespace nf4

@@ -35,7 +35,7 @@
  *     nothing has been enqueued.  NF4_ERR_HIP reports a failed launch or a
  *     failed stream-ordered allocation (hipGetLastError); the stream's later
  *     work is then undefined.
- *   - State kept across calls: the split-N workspace of nf4_grad_a, one
+ *   - State kept across calls: the workspace of nf4_grad_a / nf4_forward, one
  *     device buffer per (device, stream) that has needed one, grown on
  *     demand and held until nf4_release_workspaces().  Calls on one stream
  *     share it (they run in order); concurrent calls on different streams
@@ -134,6 +134,35 @@ int nf4_grad_a_plan(int64_t M, int64_t N, int64_t K, int* out5);
  */
 int nf4_grad_a_forced(const float* grad_out, const float* scales, const uint8_t* codes, float* grad_a,
                       int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, hipStream_t stream);
+
+/*
+ * nf4_forward -- the forward product of the same frozen layer (the subject
+ * page's header comment: the backward kernel is the analog of the forward
+ * C = A @ B over the shared dimension K, B_nf4 being K x N):
+ *
+ *   a      : const float   [M][K]    activations
+ *   scales : const float   [N][K/64]  } the same packed weight as nf4_grad_a
+ *   codes  : const uint8_t [N][K/2]   }
+ *   c      : float         [M][N], OVERWRITTEN
+ *
+ *   c[m][n] = sum_k fp16(a[m][k]) * fp16(w[n][k]), accumulated in fp32, with
+ *   fp16() round-to-nearest-even and w the fp32 dequantised weight.  Requires
+ *   K % 64 == 0 and N % 8 == 0 (NF4_ERR_SHAPE otherwise), and a, codes below
+ *   2 GiB.  M == 0 or N == 0 enqueues nothing; K == 0 writes zeros.  Bitwise
+ *   deterministic for a given (M, N, K).  Uses the stream's workspace (see the
+ *   shared rules) for an fp16 copy of `a` (2 * 16*ceil(M/16) * K bytes) and,
+ *   when K is split, fp32 partials.
+ */
+int nf4_forward(const float* a, const float* scales, const uint8_t* codes, float* c,
+                int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * nf4_forward_forced -- nf4_forward with the number of K chunks forced
+ * (`splits` >= 1, rounded so that every chunk is a whole number of 64-wide
+ * stages); for tests and tuning.  Same contract as nf4_forward.
+ */
+int nf4_forward_forced(const float* a, const float* scales, const uint8_t* codes, float* c,
+                       int64_t M, int64_t N, int64_t K, int splits, hipStream_t stream);
 
 /*
  * nf4_release_workspaces -- frees every cached split-N workspace.  It first

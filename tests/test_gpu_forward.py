@@ -1,0 +1,167 @@
+"""GPU parity of the forward product nf4_forward against the CPU oracle.
+
+c[m][n] = sum_k fp16(a[m][k]) * fp16(w[n][k]) accumulated in fp32; accepted
+when |gpu - ref| <= 2e-3 * S + 1e-6 element by element (ref the fp64
+definition, S = sum_k |a * w|), the same bound as grad_A.  The diagnostic
+against the fp16-operand product sum_k fp16(a) * fp16(w) (fp64) leaves only
+fp32 accumulation, bounded by (K/8 + 64) * 2^-24 * S16.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def fwd_inputs(M, N, K, seed):
+    b = synth.random_code_bytes(N, K, seed)
+    s = synth.random_scales_uniform(N, K, seed + 1)
+    a = synth.grad_out_normal(M, K, seed + 2)
+    return a, s, b
+
+
+def check_forward(nb, a, s, b, M, N, K, splits=0, rows=None, what=""):
+    out = nb.forward(dev(a), dev(s), dev(b), splits=splits)
+    gpu = host(out)
+    if rows is not None:
+        gpu = gpu[rows]
+    ref, S = oracle.forward(a, s, b, M, N, K, rows=rows)
+    err = np.abs(gpu.astype(np.float64) - ref)
+    lim = 2e-3 * S + 1e-6
+    if (err > lim).any():
+        i = np.unravel_index(np.argmax(err / lim), err.shape)
+        raise AssertionError(f"{what}: {int((err > lim).sum())} out of bound; worst at {i}: gpu={gpu[i]!r} "
+                             f"ref={ref[i]!r} S={S[i]!r}")
+    assert np.all(np.isfinite(gpu))
+    # fp16-operand diagnostic
+    w16 = oracle.dequant(s, b, N, K).astype(np.float16).astype(np.float64)
+    a16 = (a if rows is None else a[rows]).astype(np.float16).astype(np.float64)
+    ref16, S16 = a16 @ w16.T, np.abs(a16) @ np.abs(w16).T
+    tol = (K / 8 + 64) * 2.0 ** -24 * S16 + 1e-30
+    err16 = np.abs(gpu.astype(np.float64) - ref16)
+    if (err16 > tol).any():
+        i = np.unravel_index(np.argmax(err16 / np.maximum(tol, 1e-300)), err16.shape)
+        raise AssertionError(f"{what}: fp16-operand diagnostic failed at {i}: gpu={gpu[i]!r} ref16={ref16[i]!r}")
+    return gpu
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 8, 64), (5, 24, 128), (17, 136, 192), (512, 128, 64), (513, 256, 640),
+                                   (700, 1000, 448), (1030, 264, 1088), (64, 256, 256)])
+def test_forward_ragged_shapes(lib, M, N, K):
+    """Ragged M (fragment rows padded to 16, tile rows past M), N not a multiple of the 128-column tile,
+    single-stage and many-stage reductions, the default split choice."""
+    a, s, b = fwd_inputs(M, N, K, seed=M + 3 * N + 7 * K)
+    check_forward(lib, a, s, b, M, N, K, what=f"forward {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5])
+@pytest.mark.parametrize("M,N,K", [(300, 256, 1024), (64, 128, 3584), (40, 48, 320)])
+def test_forward_split_k(lib, splits, M, N, K):
+    a, s, b = fwd_inputs(M, N, K, seed=11 * M + N + K + splits)
+    check_forward(lib, a, s, b, M, N, K, splits=splits, what=f"forward s{splits} {M}x{N}x{K}")
+
+
+def test_forward_attention_projection_config(lib):
+    """The attention-projection layer (K = N = 1536) at M = 2048, oracle-packed N(0, 0.02) weights,
+    activations N(0, 1), every output checked."""
+    M, N, K = 2048, 1536, 1536
+    w = synth.weights_normal(N, K, 0)
+    s, b = oracle.pack(w, N, K)
+    a = synth.grad_out_normal(M, K, seed=5)
+    check_forward(lib, a, s, b, M, N, K, what="forward attn proj")
+
+
+@pytest.mark.parametrize("N,K", [(3584, 3584), (18944, 3584), (3584, 18944)])
+def test_forward_full_step_shapes_sampled_rows(lib, N, K):
+    """Full-step layer shapes at M = 8192 in the launch configuration the planner picks; 16 sampled
+    rows checked against the oracle (row-wise exact definition)."""
+    M = 8192
+    b = synth.random_code_bytes(N, K, seed=N + K)
+    s = synth.random_scales_uniform(N, K, seed=N + K + 1)
+    a = synth.grad_out_normal(M, K, seed=N + K + 2, std=1e-2)
+    rows = np.random.default_rng(N + K).choice(M, size=16, replace=False)
+    rows.sort()
+    check_forward(lib, a, s, b, M, N, K, rows=rows, what=f"forward 8192x{N}x{K}")
+
+
+def test_forward_deterministic(lib):
+    M, N, K = 600, 512, 1536
+    a, s, b = fwd_inputs(M, N, K, seed=91)
+    ad, sd, bd = dev(a), dev(s), dev(b)
+    for splits in (0, 1, 3):
+        r1 = host(lib.forward(ad, sd, bd, splits=splits))
+        r2 = host(lib.forward(ad, sd, bd, splits=splits))
+        assert np.array_equal(r1.view(np.uint32), r2.view(np.uint32))
+
+
+def test_forward_one_hot_rows_give_fp16_weight_columns(lib):
+    M, N, K = 9, 136, 320
+    b = synth.random_code_bytes(N, K, seed=93)
+    s = synth.random_scales_uniform(N, K, seed=94)
+    a = np.zeros((M, K), dtype=np.float32)
+    picks = np.random.default_rng(95).integers(0, K, size=M)
+    a[np.arange(M), picks] = 1.0
+    gpu = host(lib.forward(dev(a), dev(s), dev(b)))
+    w16 = oracle.dequant(s, b, N, K).astype(np.float16).astype(np.float32)
+    assert np.array_equal(gpu, w16[:, picks].T)
+
+
+def test_forward_power_of_two_scaling_is_exact(lib):
+    M, N, K = 40, 256, 512
+    a, s, b = fwd_inputs(M, N, K, seed=97)
+    a = (np.sign(a) * np.clip(np.abs(a), 2.0 ** -12, 1000.0)).astype(np.float32)  # fp16 images stay normal
+    base = host(lib.forward(dev(a), dev(s), dev(b)))
+    assert np.array_equal(host(lib.forward(dev(a * 2), dev(s), dev(b))), base * 2)
+    assert np.array_equal(host(lib.forward(dev(a), dev(s * np.float32(0.5)), dev(b))), base * 0.5)
+
+
+def test_forward_and_grad_a_are_adjoint_on_the_gpu(lib):
+    """<forward(A), X> = <A, grad_a(X)> up to the two products' bounds."""
+    M, N, K = 48, 704, 384
+    b = synth.random_code_bytes(N, K, seed=98)
+    s = synth.random_scales_uniform(N, K, seed=99)
+    a = synth.grad_out_normal(M, K, seed=100)
+    x = synth.grad_out_normal(M, N, seed=101)
+    c = host(lib.forward(dev(a), dev(s), dev(b))).astype(np.float64)
+    ga = host(lib.grad_a(dev(x), dev(s), dev(b))).astype(np.float64)
+    _, Sf = oracle.forward(a, s, b, M, N, K)
+    _, Sg = oracle.grad_a(x, s, b, M, N, K)
+    lhs = np.sum(c * x)
+    rhs = np.sum(a.astype(np.float64) * ga)
+    lim = np.sum(np.abs(x) * (2e-3 * Sf + 1e-6)) + np.sum(np.abs(a) * (2e-3 * Sg + 1e-6))
+    assert abs(lhs - rhs) <= lim
+
+
+def test_forward_empty_and_rejected_shapes(lib):
+    s = dev(np.ones((8, 1), dtype=np.float32))
+    b = dev(np.full((8, 32), 0xFF, dtype=np.uint8))
+    # K == 0: an empty sum, zeros written
+    out = dev(np.full((3, 8), 7.0, dtype=np.float32))
+    lib.forward(dev(np.zeros((3, 0), dtype=np.float32)), dev(np.zeros((8, 0), dtype=np.float32)),
+                dev(np.zeros((8, 0), dtype=np.uint8)), out=out)
+    assert np.all(host(out) == 0.0)
+    # M == 0: nothing to do
+    r = lib.forward(dev(np.zeros((0, 64), dtype=np.float32)), s, b)
+    assert tuple(r.shape) == (0, 8)
+    # N % 8 != 0 and K % 64 != 0 are rejected before any launch
+    with pytest.raises(lib.Nf4Error):
+        lib.forward(dev(np.ones((2, 64), dtype=np.float32)), dev(np.ones((4, 1), dtype=np.float32)),
+                    dev(np.zeros((4, 32), dtype=np.uint8)))
+    st = lib._lib.nf4_forward(dev(np.ones((2, 96), dtype=np.float32)).data_ptr(), s.data_ptr(), b.data_ptr(),
+                              dev(np.zeros((2, 8), dtype=np.float32)).data_ptr(), 2, 8, 96,
+                              torch.cuda.current_stream().cuda_stream)
+    assert st == lib.NF4_ERR_SHAPE
