@@ -97,10 +97,10 @@ def kernel_name_for(plan, N=None):
     if plan["kernel"] == "zero_fill":
         return "fill_zero_kernel"
     if plan["kernel"] == "wide":
-        return "grad_a_wide_kernel<%d, 0>" % plan["rb"]
+        return "grad_a_wide_kernel<%d, 0, false>" % plan["rb"]
     if plan["kernel"] == "wide16":
         # two kernels per call: the fp16 A-fragment pass, then the wide kernel reading the fragments
-        return "grad_out_frag_kernel<false>+grad_a_wide_kernel<1, 3>"
+        return "grad_out_frag_kernel<false>+grad_a_wide_kernel<1, 3, false>"
     if plan["kernel"] == "stream":
         return "grad_a_stream_kernel<true>" if N is not None and N % 4 == 0 else "grad_a_stream_kernel<false>"
     if plan["rb"] == 2 and N is not None and N % 64 == 0:
@@ -157,7 +157,8 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "copies": 3}), flush=True)
 
 
-def time_config(torch, nb, M, N, K, seed, g_std, rotate_bytes=512 << 20, target_s=0.02, trials=5, op="grad_a"):
+def time_config(torch, nb, M, N, K, seed, g_std, rotate_bytes=512 << 20, target_s=0.02, trials=5, op="grad_a",
+                splits=1):
     """Median per-call time of nf4_grad_a (or, op="forward", nf4_forward) over rotated input sets (each set:
     codes, scales, grad_out [M][N] or activations [M][K])."""
     per_set = alg_bytes(M, N, K)
@@ -177,7 +178,13 @@ def time_config(torch, nb, M, N, K, seed, g_std, rotate_bytes=512 << 20, target_
             g = torch.empty((M, N), device="cuda").normal_(0.0, g_std, generator=gen)
             o = torch.empty((M, K), device="cuda")
         sets.append((g, s, c, o))
-    call = nb.forward if op == "forward" else nb.grad_a
+    if op == "forward":
+        call = nb.forward
+    elif op == "unfused":
+        def call(g, s, c, out):
+            return nb.grad_a_forced(g, s, c, "unfused", rb=1, splits=splits, out=out)
+    else:
+        call = nb.grad_a
     torch.cuda.synchronize()
     for i in range(5):
         g, s, c, o = sets[i % nsets]
@@ -203,6 +210,36 @@ def time_config(torch, nb, M, N, K, seed, g_std, rotate_bytes=512 << 20, target_
     torch.cuda.empty_cache()
     res.sort()
     return res[len(res) // 2], res[0], res[-1], nsets
+
+
+def unfused_splits(M, N, K):
+    """N-chunk count for the unfused comparison path: the fused plan's for the large-M tile plans; for a
+    skinny M, enough chunks to give every CU a 512 x 128 tile (the path has no skinny kernel)."""
+    tiles = -(-M // 512) * -(-K // 128)
+    return max(1, min(N // 64, 256 // tiles)) if tiles < 256 else 1
+
+
+def per_config_unfused(torch, nb):
+    """Fused (the default plan) against the unfused comparison path -- the weights dequantised to fp16 by a
+    separate pass, then the same GEMM copying them instead of decoding (bitwise the same result) -- on the
+    configuration shapes and the full-step layer shapes."""
+    import synth
+    shapes = (synth.CONFIGS["attn_proj"] + synth.CONFIGS["mlp_pair"] + synth.SKINNY_SHAPES +
+              [synth.Shape(f"full_step_{p}", M_STEP, N, K) for (p, N, K) in PROJ if p in ("q", "k", "gate", "down")])
+    out = {}
+    for i, shp in enumerate(shapes):
+        gstd = 1.0 if shp.M <= 16 else 1e-2
+        fused, _, _, _ = time_config(torch, nb, shp.M, shp.N, shp.K, seed=i, g_std=gstd)
+        plan = nb.grad_a_plan(shp.M, shp.N, shp.K)
+        sp = plan["splits"] if plan["kernel"] in ("wide", "wide16") else unfused_splits(shp.M, shp.N, shp.K)
+        unf, _, _, nsets = time_config(torch, nb, shp.M, shp.N, shp.K, seed=i, g_std=gstd, op="unfused", splits=sp)
+        fl = 2.0 * shp.M * shp.N * shp.K
+        out[shp.name] = {"M": shp.M, "N": shp.N, "K": shp.K, "fused_us": round(fused * 1e6, 2),
+                         "unfused_us": round(unf * 1e6, 2), "unfused_over_fused": round(unf / fused, 3),
+                         "fused_tflops": round(fl / fused / 1e12, 2), "unfused_tflops": round(fl / unf / 1e12, 2),
+                         "fused_plan": plan["kernel"], "unfused_splits": sp, "rotated_input_sets": nsets}
+        log(f"[bench] unfused {shp.name}: fused {fused * 1e6:.1f} us, unfused {unf * 1e6:.1f} us")
+    return out
 
 
 def per_config_table(torch, nb, op="grad_a"):
@@ -284,6 +321,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config table")
+    ap.add_argument("--unfused-configs", action="store_true",
+                    help="only the fused-against-unfused comparison table (one JSON line)")
     ap.add_argument("--forward-configs", action="store_true",
                     help="only the forward product's per-config table and its CPU oracle baseline (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -300,6 +339,9 @@ def main():
         return
     import dequant_backward_gemm_amd as nb
 
+    if args.unfused_configs:
+        print(json.dumps({"per_config_unfused": per_config_unfused(torch, nb)}), flush=True)
+        return
     if args.forward_configs:
         rec = {"per_config_forward": per_config_table(torch, nb, op="forward"),
                "cpu_baseline_forward": None if args.no_cpu else cpu_baseline(target_s=5.0, op="forward")}

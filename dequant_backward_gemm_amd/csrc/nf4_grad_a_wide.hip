@@ -126,13 +126,53 @@ __global__ __launch_bounds__(256) void grad_out_frag_kernel(const float* __restr
   }
 }
 
-template <int WC, int AF>
+// Unfused comparison path, first pass: the weights dequantised to fp16 once,
+// written in exactly the LDS fragment layout the wide kernel's decode role
+// produces for a stage (tile width 128): block (k-tile kt, stage of 64 rows
+// st) is 16 KiB at (kt * N/64 + st) * 16 KiB.  Same decode arithmetic,
+// fp16(fl32(scale * level)), computed per weight; columns past K are zero.
+__global__ __launch_bounds__(512) void dequant_bfrag_kernel(const float* __restrict__ S,
+                                                            const uint32_t* __restrict__ C32,
+                                                            uint32_t* __restrict__ F, int N, int K) {
+  __shared__ float lv[16];
+  const int tid = threadIdx.x;
+  if (tid < 16) lv[tid] = kLevels[tid];
+  __syncthreads();
+  const int nstg = N / 64;
+  const int kt = blockIdx.x / nstg, st = blockIdx.x % nstg;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int p = lane & 3, dl = lane >> 2;
+  const int nr0 = 64 * st + 32 * (wave >> 2) + 16 * (p >> 1) + 4 * (wave & 3) + 2 * (p & 1);
+  const int col0 = 128 * kt + 8 * dl;
+  uint32_t x[2] = {0u, 0u};
+  float sc[2] = {0.f, 0.f};
+  if (col0 < K) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      x[r] = C32[((size_t)(nr0 + r) * (size_t)K + (size_t)col0) / 8];
+      sc[r] = S[(size_t)(nr0 + r) * (size_t)(K / 64) + (size_t)(col0 / 64)];
+    }
+  }
+  uint32_t* dst = F + ((size_t)kt * nstg + st) * 4096 + (size_t)(wave >> 2) * 2048 +
+                  (size_t)(dl + 16 * (wave & 3)) * 4 + (size_t)p;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float w0 = sc[0] * lv[(x[0] >> (4 * c)) & 15u];
+    const float w1 = sc[1] * lv[(x[1] >> (4 * c)) & 15u];
+    dst[c * 256] = pack_half2_rne(w0, w1);
+  }
+}
+
+template <int WC, int AF, bool BCOPY = false>
 __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
     const void* __restrict__ Gv, const float* __restrict__ S, const uint32_t* __restrict__ C32,
     float* __restrict__ out, int M, int N, int K, int n_chunk, int tiles_m, int tiles_k) {
   // AF == 0: Gv is grad_out (fp32 [M][N]); AF > 0: Gv holds the fp16 A
   // fragments of grad_out_frag_kernel and AF k-steps of them are in flight.
+  // BCOPY: C32 holds the fp16 B fragments of dequant_bfrag_kernel, which are
+  // copied into the LDS fragment buffers instead of decoded (S is unused).
   static_assert(AF == 0 || AF == 1 || AF == 3, "fragment prefetch depth 1 or 3");
+  static_assert(!BCOPY || (WC == 1 && AF > 0), "fragment copy: 128-column tiles, A fragments");
   const float* __restrict__ G = static_cast<const float*>(Gv);
   using Cfg = WideCfg<WC>;
   constexpr int WR = Cfg::WR, BM = Cfg::BM, BK = Cfg::BK, KB = Cfg::KB;
@@ -155,7 +195,8 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
   const int ne = min(N, nb + n_chunk);
   const int nst = (ne - nb) >> 6;
 
-  const __amdgpu_buffer_rsrc_t rc = make_rsrc(C32, (uint32_t)((size_t)N * (size_t)K / 2));
+  const __amdgpu_buffer_rsrc_t rc =
+      make_rsrc(C32, BCOPY ? (uint32_t)((size_t)tiles_k * (size_t)(N / 64) * 16384u) : (uint32_t)((size_t)N * (size_t)K / 2));
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, (uint32_t)((size_t)N * (size_t)(K / 64) * 4));
   const int mpad = (M + 15) & ~15;
   const __amdgpu_buffer_rsrc_t rg =
@@ -346,12 +387,34 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
   constexpr int NAB = AF ? AF + 1 : 1;  // fragment buffers in the ring
   u32x4 afr[NAB][4];
 
+  // fragment copy (BCOPY): thread tid moves bytes 16 tid and 8192 + 16 tid of a stage's 16 KiB
+  auto load_bf = [&](int st, u32x4 (&x)[2]) {
+    const uint32_t off = ((uint32_t)kt * (uint32_t)(N / 64) + stage_row(st) / 64u) * 16384u;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      x[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, 16u * (uint32_t)tid + 8192u * h, off, 0));
+  };
+  auto store_bf = [&](uint32_t foff, const u32x4 (&x)[2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) lds_store_u32x4(smem, Cfg::kFragBase + foff + 16u * (uint32_t)tid + 8192u * h, x[h]);
+  };
+  u32x4 bfx[2];  // B fragments of the stage copied during the current one (BCOPY)
+
   float ar[8][4];       // grad_out of the next k-step, as loaded
   uint32_t xc[WC][2];   // codes of the stage decoded during the current one
   float sc[WC];         // scales of the tables built during the current stage
 
-  // Prologue: tables of stages 0 and 1, stage 0 decoded into fragment buffer 0.
-  {
+  // Prologue: tables of stages 0 and 1, stage 0 decoded into fragment buffer 0
+  // (or, BCOPY, stage 0 copied into it and stage 1 loaded).
+  if constexpr (BCOPY) {
+    u32x4 b0[2];
+    load_bf(0, b0);
+    load_bf(1, bfx);
+#pragma unroll
+    for (int j = 0; j < AF; ++j) load_af(j, afr[j]);
+    store_bf(0u, b0);
+    __syncthreads();
+  } else {
     float s0[WC], s1[WC];
     uint32_t x0[WC][2];
     load_scales(0, s0);
@@ -385,7 +448,8 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
     constexpr uint32_t frd = P * kFragStage, fwr = (P ^ 1u) * kFragStage;
     uint32_t xn[WC][2];
     float scn[WC];
-    prep(xc);
+    u32x4 bfn[2];
+    if constexpr (!BCOPY) prep(xc);
     // k-step s: convert grad_out of s and issue the loads of the next k-step,
     // then 8 ticks, one per MFMA tile t (4 MFMAs, one per row block).  B
     // fragments are read three ticks ahead through a ring of four; the decode
@@ -429,20 +493,30 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
         for (int rb = 0; rb < 4; ++rb)
           acc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(af[rb]), as_half8(bf[t % 4]), acc[rb][t], 0, 0, 0);
         if constexpr (t + 3 < 8) bf[(t + 3) % 4] = read_b(t + 3);
-        if constexpr (t >= 2 && t < 6) store_col(std::integral_constant<int, c0 + t - 2>{}, fwr, lk[t & 1]);
-        if constexpr (t < 4) lookup_col(std::integral_constant<int, c0 + t>{}, toff_dec, lk[t & 1]);
-        if constexpr (t == 6 && s == 0) load_codes(st + 2, xn);
-        if constexpr (t == 6 && s == 1) load_scales(st + 3, scn);
-        if constexpr (t == 7 && s == 0) build_tables(sc, toff_build);
+        if constexpr (BCOPY) {
+          if constexpr (t == 2 && s == 0) store_bf(fwr, bfx);
+          if constexpr (t == 6 && s == 0) load_bf(st + 2, bfn);
+        } else {
+          if constexpr (t >= 2 && t < 6) store_col(std::integral_constant<int, c0 + t - 2>{}, fwr, lk[t & 1]);
+          if constexpr (t < 4) lookup_col(std::integral_constant<int, c0 + t>{}, toff_dec, lk[t & 1]);
+          if constexpr (t == 6 && s == 0) load_codes(st + 2, xn);
+          if constexpr (t == 6 && s == 1) load_scales(st + 3, scn);
+          if constexpr (t == 7 && s == 0) build_tables(sc, toff_build);
+        }
         __builtin_amdgcn_sched_barrier(0);
       });
     });
     __syncthreads();
+    if constexpr (BCOPY) {
+      bfx[0] = bfn[0];
+      bfx[1] = bfn[1];
+    } else {
 #pragma unroll
-    for (int v = 0; v < WC; ++v) {
-      xc[v][0] = xn[v][0];
-      xc[v][1] = xn[v][1];
-      sc[v] = scn[v];
+      for (int v = 0; v < WC; ++v) {
+        xc[v][0] = xn[v][0];
+        xc[v][1] = xn[v][1];
+        sc[v] = scn[v];
+      }
     }
   };
 
@@ -495,6 +569,22 @@ hipError_t launch_grad_a_wide(int wc, int grid, const float* grad_out, const flo
 }
 
 size_t wide_frag_bytes(int64_t M, int64_t N) { return (size_t)((M + 15) / 16) * 16 * (size_t)N * 2; }
+
+size_t unfused_bfrag_bytes(int64_t N, int64_t K) { return (size_t)((K + 127) / 128) * (size_t)(N / 64) * 16384; }
+
+hipError_t launch_grad_a_unfused(int grid, const float* grad_out, void* afrags, void* bfrags, const float* scales,
+                                 const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,
+                                 int tiles_k, hipStream_t stream) {
+  hipLaunchKernelGGL(dequant_bfrag_kernel, dim3(((K + 127) / 128) * (N / 64)), dim3(512), 0, stream, scales, codes,
+                     static_cast<uint32_t*>(bfrags), N, K);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_frag_pass(grad_out, afrags, M, N, /*natural=*/false, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((grad_a_wide_kernel<1, WIDE_FRAG_DEPTH, true>), dim3(grid), dim3(512), 0, stream, afrags, scales,
+                     static_cast<const uint32_t*>(bfrags), dst, M, N, K, n_chunk, tiles_m, tiles_k);
+  return hipGetLastError();
+}
 
 hipError_t launch_frag_pass(const float* src, void* frags, int rows, int cols, bool natural, hipStream_t stream) {
   const int64_t total = (int64_t)((rows + 15) / 16) * (cols / 32) * 64;

@@ -23,7 +23,8 @@ hipError_t launch_grad_a(const float* grad_out, const float* scales, const uint8
 struct GradAPlan {
   int kernel;    // 0 = tile (BM = 128 * rb), 1 = skinny (M <= 16), 2 = zero-fill (N == 0),
                  // 3 = wide (8 waves, tile (512 / rb) x (128 * rb)), 4 = stream (M <= 16),
-                 // 5 = wide fed by fp16 A fragments from a conversion pass (tile 512 x 128)
+                 // 5 = wide fed by fp16 A fragments from a conversion pass (tile 512 x 128),
+                 // 6 = unfused comparison path (fp16 weight pass, then a fragment-copy GEMM)
   int rb;        // tile: 32-row blocks per wave; wide: 128-column groups
   int splits;    // number of N-chunks (1 = no workspace, no reduce launch)
   int n_chunk;   // rows of N per chunk
@@ -61,6 +62,15 @@ size_t wide_frag_bytes(int64_t M, int64_t N);
 hipError_t launch_grad_a_wide_frag(int grid, const float* grad_out, void* frags, const float* scales,
                                    const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,
                                    int tiles_k, hipStream_t stream);
+
+// Unfused comparison path (kernel 6): the weights dequantised to fp16 once
+// into B fragments (unfused_bfrag_bytes(N, K) bytes), then the fragment-fed
+// wide kernel copying them into LDS instead of decoding.  Same preconditions
+// as the wide kernel.
+size_t unfused_bfrag_bytes(int64_t N, int64_t K);
+hipError_t launch_grad_a_unfused(int grid, const float* grad_out, void* afrags, void* bfrags, const float* scales,
+                                 const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,
+                                 int tiles_k, hipStream_t stream);
 
 // fp32 [rows][cols] -> fp16 MFMA A fragments (reduction along cols, cols % 32
 // == 0), rows padded to 16 with zeros: the backward wide kernel's permuted

@@ -222,10 +222,10 @@ bool make_plan(int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, 
     p.n_chunk = (int)chunk;
     p.splits = (int)cdiv(N, chunk);
     p.grid = (int)(cdiv(K, kStreamBK) * p.splits);
-  } else if (kernel == 5) {
+  } else if (kernel == 5 || kernel == 6) {
     if (!wide_kernel_supported(M, N, K)) return false;
     const int64_t chunk = cdiv(cdiv(N, splits), 64) * 64;
-    p.kernel = 5;
+    p.kernel = kernel;
     p.rb = 1;
     p.n_chunk = (int)chunk;
     p.splits = (int)cdiv(N, chunk);
@@ -257,17 +257,21 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
   float* dst = grad_a;
   float* ws = nullptr;
   void* frags = nullptr;
+  void* bfrags = nullptr;
   {
     // workspace: split partials, then (fragment-fed wide kernel) the fp16 A fragments
     const size_t part = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)K * sizeof(float) : 0;
     const size_t part_al = (part + 255) & ~(size_t)255;
-    const size_t frag = p.kernel == 5 ? wide_frag_bytes(M, N) : 0;
-    if (part + frag > 0) {
+    const size_t frag = (p.kernel == 5 || p.kernel == 6) ? wide_frag_bytes(M, N) : 0;
+    const size_t frag_al = (frag + 255) & ~(size_t)255;
+    const size_t bfrag = p.kernel == 6 ? unfused_bfrag_bytes(N, K) : 0;
+    if (part + frag + bfrag > 0) {
       char* base = nullptr;
-      hipError_t e = stream_workspace(stream, part_al + frag, reinterpret_cast<void**>(&base));
+      hipError_t e = stream_workspace(stream, part_al + frag_al + bfrag, reinterpret_cast<void**>(&base));
       if (e != hipSuccess) return e;
       if (part) ws = reinterpret_cast<float*>(base);
       if (frag) frags = base + part_al;
+      if (bfrag) bfrags = base + part_al + frag_al;
     }
     if (ws) dst = ws;
   }
@@ -278,6 +282,9 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
   } else if (p.kernel == 4) {
     e = launch_grad_a_stream(p.grid, grad_out, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
                              (int)cdiv(K, kStreamBK), stream);
+  } else if (p.kernel == 6) {
+    e = launch_grad_a_unfused(p.grid, grad_out, frags, bfrags, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
+                              (int)cdiv(M, wide_tile_rows(1)), (int)cdiv(K, wide_tile_cols(1)), stream);
   } else if (p.kernel == 5) {
     e = launch_grad_a_wide_frag(p.grid, grad_out, frags, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
                                 (int)cdiv(M, wide_tile_rows(1)), (int)cdiv(K, wide_tile_cols(1)), stream);

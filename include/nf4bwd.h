@@ -126,7 +126,11 @@ int nf4_grad_a_plan(int64_t M, int64_t N, int64_t K, int* out5);
  * kernel 4 = streaming (requires M <= 16 and grad_out and the codes below
  * 2 GiB; `rb` ignored), kernel 5 = wide tiled 512 x 128 fed by the fp16
  * A-fragment pass (same requirements as kernel 3; `rb` ignored; the fragments
- * take 2 * 16*ceil(M/16) * N bytes of the split-N workspace);
+ * take 2 * 16*ceil(M/16) * N bytes of the split-N workspace), kernel 6 = the
+ * unfused comparison path: the weights dequantised to fp16 by a separate pass
+ * (2 * N * 128*ceil(K/128) bytes of workspace), then the kernel-5 GEMM
+ * reading them instead of decoding (same requirements, bitwise the same
+ * result as kernel 5);
  * `splits` = requested number of N-chunks
  * (rounded so that every chunk but the last is a whole number of stages).
  * Same contract and results-to-bound as nf4_grad_a; NF4_ERR_SHAPE if the

@@ -195,6 +195,21 @@ def test_grad_a_wide16_matches_wide_bitwise(lib):
         lib.grad_a_forced(dev(g[:, :2000]), sd[:2000], bd[:2000], "wide16", rb=1)
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("M,N,K", [(17, 64, 64), (200, 384, 768), (513, 640, 320), (1030, 256, 1088)])
+def test_grad_a_unfused_matches_fused_bitwise(lib, splits, M, N, K):
+    """The unfused comparison path (weights dequantised to fp16 by a separate pass, then a GEMM that copies
+    them instead of decoding) multiplies the same fp16 operands in the same order as the fused kernel:
+    bitwise equal results, and within the oracle's bound."""
+    g, s, b = random_inputs(M, N, K, seed=3 * M + N + 5 * K + splits)
+    gd, sd, bd = dev(g), dev(s), dev(b)
+    fused = host(lib.grad_a_forced(gd, sd, bd, "wide16", rb=1, splits=splits))
+    unfused = host(lib.grad_a_forced(gd, sd, bd, "unfused", rb=1, splits=splits))
+    assert np.array_equal(fused.view(np.uint32), unfused.view(np.uint32))
+    ref, S = oracle.grad_a(g, s, b, M, N, K)
+    assert_within_bound(unfused, ref, S, f"unfused s{splits} {M}x{N}x{K}")
+
+
 def test_grad_a_wide_deterministic_and_rejects_ragged_n(lib):
     M, N, K = 700, 4096, 384
     g, s, b = random_inputs(M, N, K, seed=31)
