@@ -25,7 +25,14 @@ LIB_PATH = os.path.join(_PKG_DIR, "libnf4bwd.so")
 NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_HIP = 0, 1, 2, 3, 4
 
 EXPORTED_SYMBOLS = ("nf4_grad_a", "nf4_dequant", "nf4_pack", "nf4_status_string", "nf4_grad_a_plan",
-                    "nf4_grad_a_forced", "nf4_release_workspaces", "nf4_forward", "nf4_forward_forced")
+                    "nf4_grad_a_forced", "nf4_release_workspaces", "nf4_forward", "nf4_forward_forced",
+                    "nf4_grad_a_grouped")
+GROUP_MAX = 8
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("grad_out", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+                ("grad_a", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
 
 
 class Nf4Error(RuntimeError):
@@ -58,6 +65,8 @@ def _load() -> ctypes.CDLL:
     lib.nf4_forward.restype = ctypes.c_int
     lib.nf4_forward_forced.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp]
     lib.nf4_forward_forced.restype = ctypes.c_int
+    lib.nf4_grad_a_grouped.argtypes = [ctypes.c_void_p, ci, i64, vp]
+    lib.nf4_grad_a_grouped.restype = ctypes.c_int
     lib.nf4_release_workspaces.argtypes = []
     lib.nf4_release_workspaces.restype = ctypes.c_int
     return lib
@@ -128,6 +137,34 @@ def grad_a(grad_out, scales, codes, out=None, stream=None):
     _check(grad_a_raw(_ptr(grad_out), _ptr(scales), _ptr(codes), _ptr(out), M, N, K, _stream_handle(stream)),
            "nf4_grad_a")
     return out
+
+
+def grad_a_grouped(problems, outs=None, stream=None):
+    """grad_A of several problems sharing M in as few launches as possible.
+
+    problems: sequence of (grad_out [M, N], scales [N, K/64], codes [N, K/2]); returns the list of grad_A
+    [M, K] tensors (or fills `outs`)."""
+    import torch
+    if len(problems) > GROUP_MAX:
+        raise ValueError(f"at most {GROUP_MAX} problems per group")
+    arr = (_Problem * max(1, len(problems)))()
+    res = []
+    M = problems[0][0].shape[0] if problems else 0
+    for i, (g, s, c) in enumerate(problems):
+        Mi, N = g.shape
+        K = c.shape[1] * 2
+        if Mi != M:
+            raise ValueError("all problems of a group share M")
+        _require(g, torch.float32, (M, N), "grad_out")
+        _require(s, torch.float32, (N, K // 64), "scales")
+        _require(c, torch.uint8, (N, K // 2), "codes")
+        o = outs[i] if outs is not None else torch.empty((M, K), dtype=torch.float32, device=g.device)
+        _require(o, torch.float32, (M, K), "out")
+        arr[i] = _Problem(_ptr(g), _ptr(s), _ptr(c), _ptr(o), N, K)
+        res.append(o)
+    _check(_lib.nf4_grad_a_grouped(ctypes.cast(arr, ctypes.c_void_p), len(problems), M, _stream_handle(stream)),
+           "nf4_grad_a_grouped")
+    return res
 
 
 def grad_a_forced(grad_out, scales, codes, kernel: str, rb: int = 2, splits: int = 1, out=None, stream=None):

@@ -100,6 +100,36 @@ int nf4_forward_forced(const float* a, const float* scales, const uint8_t* codes
   return forward_checked(a, scales, codes, c, M, N, K, splits, stream);
 }
 
+int nf4_grad_a_grouped(const nf4_grad_a_problem* problems, int count, int64_t M, hipStream_t stream) {
+  if (count < 0 || count > NF4_GROUP_MAX) return NF4_ERR_SHAPE;
+  if (count > 0 && problems == nullptr) return NF4_ERR_NULL;
+  if (M < 0) return NF4_ERR_SHAPE;
+  const float* g[NF4_GROUP_MAX];
+  const float* sc[NF4_GROUP_MAX];
+  const uint8_t* cd[NF4_GROUP_MAX];
+  float* out[NF4_GROUP_MAX];
+  int64_t n[NF4_GROUP_MAX], k[NF4_GROUP_MAX];
+  for (int i = 0; i < count; ++i) {
+    const nf4_grad_a_problem& p = problems[i];
+    const int64_t N = p.N, K = p.K;
+    if (!dims_ok(M, N) || !dims_ok(N, K) || !dims_ok(M, K) || (K % 64) != 0) return NF4_ERR_SHAPE;
+    if (M > 0 && K > 0) {
+      if (p.grad_a == nullptr) return NF4_ERR_NULL;
+      if (N > 0 && (p.grad_out == nullptr || p.scales == nullptr || p.codes == nullptr)) return NF4_ERR_NULL;
+      if (!aligned16(p.grad_a) || (N > 0 && (!aligned16(p.grad_out) || !aligned16(p.scales) || !aligned16(p.codes))))
+        return NF4_ERR_ALIGN;
+    }
+    g[i] = p.grad_out;
+    sc[i] = p.scales;
+    cd[i] = p.codes;
+    out[i] = p.grad_a;
+    n[i] = N;
+    k[i] = K;
+  }
+  if (M == 0 || count == 0) return NF4_OK;
+  return from_hip(nf4::launch_grad_a_grouped(g, sc, cd, out, n, k, count, M, stream));
+}
+
 int nf4_release_workspaces(void) { return from_hip(nf4::release_workspaces()); }
 
 const char* nf4_status_string(int status) {

@@ -163,10 +163,12 @@ __global__ __launch_bounds__(512) void dequant_bfrag_kernel(const float* __restr
   }
 }
 
-template <int WC, int AF, bool BCOPY = false>
-__global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
-    const void* __restrict__ Gv, const float* __restrict__ S, const uint32_t* __restrict__ C32,
-    float* __restrict__ out, int M, int N, int K, int n_chunk, int tiles_m, int tiles_k) {
+// One workgroup's tile of the wide kernel; `logical` is its tile index in the
+// (k-tile fastest, then m-tile, then N-chunk) order.
+template <int WC, int AF, bool BCOPY>
+__device__ __forceinline__ void wide_tile(const void* __restrict__ Gv, const float* __restrict__ S,
+                                          const uint32_t* __restrict__ C32, float* __restrict__ out, int M, int N,
+                                          int K, int n_chunk, int tiles_m, int tiles_k, int logical) {
   // AF == 0: Gv is grad_out (fp32 [M][N]); AF > 0: Gv holds the fp16 A
   // fragments of grad_out_frag_kernel and AF k-steps of them are in flight.
   // BCOPY: C32 holds the fp16 B fragments of dequant_bfrag_kernel, which are
@@ -185,7 +187,6 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
   const int ci = lane & 15, q = lane >> 4;  // MFMA lane: row / column index, quarter
   const int wr = wave % WR, wc = wave / WR;
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = logical % tiles_k;
   const int rest = logical / tiles_k;
   const int mt = rest % tiles_m;
@@ -548,6 +549,46 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
   }
 }
 
+template <int WC, int AF, bool BCOPY = false>
+__global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
+    const void* __restrict__ Gv, const float* __restrict__ S, const uint32_t* __restrict__ C32,
+    float* __restrict__ out, int M, int N, int K, int n_chunk, int tiles_m, int tiles_k) {
+  wide_tile<WC, AF, BCOPY>(Gv, S, C32, out, M, N, K, n_chunk, tiles_m, tiles_k, xcd_remap(blockIdx.x, gridDim.x));
+}
+
+// Grouped launch: the tiles of up to kWideGroupMax problems sharing M (each
+// fed by its fp16 A fragments, no N split) in one grid.  The host orders the
+// problems longest reduction first.  Tiles are dealt to the 8 XCDs in groups
+// of 8 consecutive tiles (8 k-tiles of one m-tile, which share grad_out
+// fragments in that XCD's L2), group g to XCD g % 8, so that every XCD works
+// through its share in the same longest-first order and gets a balanced mix.
+// Workgroups past the last tile (the grid is padded to whole rounds of
+// groups) return at once.
+__global__ __launch_bounds__(512, 1) void grad_a_wide_grouped_kernel(WideGroup g) {
+  const int b = blockIdx.x;
+  const int x = b & 7, slot = b >> 3;
+  const int tile = ((slot >> 3) * 8 + x) * 8 + (slot & 7);
+  if (tile >= g.total) return;
+  const void* frags = g.p[0].frags;
+  const float* scales = g.p[0].scales;
+  const uint32_t* codes = g.p[0].codes;
+  float* out = g.p[0].out;
+  int N = g.p[0].N, K = g.p[0].K, tiles_k = g.p[0].tiles_k, begin = 0;
+#pragma unroll
+  for (int j = 1; j < kWideGroupMax; ++j)
+    if (j < g.count && tile >= g.p[j].tile_begin) {
+      frags = g.p[j].frags;
+      scales = g.p[j].scales;
+      codes = g.p[j].codes;
+      out = g.p[j].out;
+      N = g.p[j].N;
+      K = g.p[j].K;
+      tiles_k = g.p[j].tiles_k;
+      begin = g.p[j].tile_begin;
+    }
+  wide_tile<1, WIDE_FRAG_DEPTH, false>(frags, scales, codes, out, g.M, N, K, N, g.tiles_m, tiles_k, tile - begin);
+}
+
 bool wide_kernel_supported(int64_t M, int64_t N, int64_t K) {
   return N > 0 && (N % 64) == 0 && (uint64_t)M * (uint64_t)N * 4 < (1ull << 31) &&
          (uint64_t)N * (uint64_t)K / 2 < (1ull << 31);
@@ -571,6 +612,13 @@ hipError_t launch_grad_a_wide(int wc, int grid, const float* grad_out, const flo
 size_t wide_frag_bytes(int64_t M, int64_t N) { return (size_t)((M + 15) / 16) * 16 * (size_t)N * 2; }
 
 size_t unfused_bfrag_bytes(int64_t N, int64_t K) { return (size_t)((K + 127) / 128) * (size_t)(N / 64) * 16384; }
+
+hipError_t launch_grad_a_wide_grouped(const WideGroup& g, hipStream_t stream) {
+  const int groups = (g.total + 7) / 8;
+  const int grid = ((groups + 7) / 8) * 64;
+  hipLaunchKernelGGL(grad_a_wide_grouped_kernel, dim3(grid), dim3(512), 0, stream, g);
+  return hipGetLastError();
+}
 
 hipError_t launch_grad_a_unfused(int grid, const float* grad_out, void* afrags, void* bfrags, const float* scales,
                                  const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,

@@ -63,6 +63,26 @@ hipError_t launch_grad_a_wide_frag(int grid, const float* grad_out, void* frags,
                                    const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,
                                    int tiles_k, hipStream_t stream);
 
+// Grouped launch of the fragment-fed wide kernel (512 x 128 tiles, no N split)
+// over several problems sharing M; problems[i].tile_begin is the index of its
+// first tile in the group's tile order (prefix sums of tiles_m * tiles_k).
+constexpr int kWideGroupMax = 8;
+struct WideProblem {
+  const void* frags;  // fp16 A fragments of this problem's grad_out
+  const float* scales;
+  const uint32_t* codes;
+  float* out;
+  int N, K, tiles_k, tile_begin;
+};
+struct WideGroup {
+  WideProblem p[kWideGroupMax];
+  int count, M, tiles_m, total;
+};
+hipError_t launch_grad_a_wide_grouped(const WideGroup& g, hipStream_t stream);
+hipError_t launch_grad_a_grouped(const float* const* grad_out, const float* const* scales,
+                                 const uint8_t* const* codes, float* const* grad_a, const int64_t* N,
+                                 const int64_t* K, int count, int64_t M, hipStream_t stream);
+
 // Unfused comparison path (kernel 6): the weights dequantised to fp16 once
 // into B fragments (unfused_bfrag_bytes(N, K) bytes), then the fragment-fed
 // wide kernel copying them into LDS instead of decoding.  Same preconditions

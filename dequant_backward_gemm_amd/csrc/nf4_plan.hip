@@ -353,4 +353,58 @@ hipError_t launch_nf4_forward(const float* a, const float* scales, const uint8_t
   return e;
 }
 
+// Grouped grad_A: problems the fragment-fed wide kernel takes (M > 16, N % 64
+// == 0, operands below 2 GiB) run as one grid, longest reduction first;
+// every other problem runs through its own nf4_grad_a plan.  Each grouped
+// problem's grad_out goes through its own fragment pass first (the fragments
+// of all of them share the stream's workspace).
+hipError_t launch_grad_a_grouped(const float* const* grad_out, const float* const* scales,
+                                 const uint8_t* const* codes, float* const* grad_a, const int64_t* N,
+                                 const int64_t* K, int count, int64_t M, hipStream_t stream) {
+  int idx[kWideGroupMax];
+  int ng = 0;
+  for (int i = 0; i < count; ++i) {
+    if (K[i] == 0) continue;
+    if (M > 16 && ng < kWideGroupMax && wide_kernel_supported(M, N[i], K[i])) {
+      idx[ng++] = i;
+    } else {
+      hipError_t e = launch_grad_a(grad_out[i], scales[i], codes[i], grad_a[i], M, N[i], K[i], stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  if (ng == 0) return hipSuccess;
+  // longest reduction (largest N) first, ties in call order
+  std::stable_sort(idx, idx + ng, [&](int a, int b) { return N[a] > N[b]; });
+  size_t off[kWideGroupMax], total_bytes = 0;
+  for (int j = 0; j < ng; ++j) {
+    off[j] = total_bytes;
+    total_bytes += (wide_frag_bytes(M, N[idx[j]]) + 255) & ~(size_t)255;
+  }
+  char* base = nullptr;
+  hipError_t e = stream_workspace(stream, total_bytes, reinterpret_cast<void**>(&base));
+  if (e != hipSuccess) return e;
+  WideGroup g{};
+  g.count = ng;
+  g.M = (int)M;
+  g.tiles_m = (int)cdiv(M, wide_tile_rows(1));
+  int begin = 0;
+  for (int j = 0; j < ng; ++j) {
+    const int i = idx[j];
+    e = launch_frag_pass(grad_out[i], base + off[j], (int)M, (int)N[i], /*natural=*/false, stream);
+    if (e != hipSuccess) return e;
+    WideProblem& w = g.p[j];
+    w.frags = base + off[j];
+    w.scales = scales[i];
+    w.codes = reinterpret_cast<const uint32_t*>(codes[i]);
+    w.out = grad_a[i];
+    w.N = (int)N[i];
+    w.K = (int)K[i];
+    w.tiles_k = (int)cdiv(K[i], wide_tile_cols(1));
+    w.tile_begin = begin;
+    begin += g.tiles_m * w.tiles_k;
+  }
+  g.total = begin;
+  return launch_grad_a_wide_grouped(g, stream);
+}
+
 }  // namespace nf4

@@ -140,6 +140,33 @@ int nf4_grad_a_forced(const float* grad_out, const float* scales, const uint8_t*
                       int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, hipStream_t stream);
 
 /*
+ * nf4_grad_a_grouped -- up to NF4_GROUP_MAX grad_A problems that share M (for
+ * example a layer's projections) in as few launches as possible: every
+ * problem the large-M wide kernel takes (M > 16, N % 64 == 0, grad_out and
+ * codes below 2 GiB) runs in one grid, the tiles of the longest reductions
+ * first, which keeps the CUs busy where separate launches end in a part-full
+ * round; any other problem runs as nf4_grad_a would run it.  Each problem's
+ * fields mean what nf4_grad_a's arguments mean, with the same layout,
+ * ownership and bound; results are bitwise equal to nf4_grad_a_forced with
+ * kernel 5 and one N-chunk for the grouped problems, and to nf4_grad_a for the
+ * others.  The grad_a arrays must not alias each other or any input.  The
+ * fp16 fragments of all grouped grad_outs share the stream's workspace
+ * (sum of 2 * 16*ceil(M/16) * N bytes).  NF4_ERR_SHAPE if count is outside
+ * 0..NF4_GROUP_MAX or a problem's shape is invalid; nothing is enqueued on
+ * any argument error.
+ */
+#define NF4_GROUP_MAX 8
+typedef struct nf4_grad_a_problem {
+  const float* grad_out;  /* [M][N] */
+  const float* scales;    /* [N][K/64] */
+  const uint8_t* codes;   /* [N][K/2] */
+  float* grad_a;          /* [M][K], overwritten */
+  int64_t N;
+  int64_t K;
+} nf4_grad_a_problem;
+int nf4_grad_a_grouped(const nf4_grad_a_problem* problems, int count, int64_t M, hipStream_t stream);
+
+/*
  * nf4_forward -- the forward product of the same frozen layer (the subject
  * page's header comment: the backward kernel is the analog of the forward
  * C = A @ B over the shared dimension K, B_nf4 being K x N):

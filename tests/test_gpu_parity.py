@@ -210,6 +210,40 @@ def test_grad_a_unfused_matches_fused_bitwise(lib, splits, M, N, K):
     assert_within_bound(unfused, ref, S, f"unfused s{splits} {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M", [17, 600, 1100])
+def test_grad_a_grouped_matches_separate_calls(lib, M):
+    """A layer-like group: problems with different N and K (one the wide kernel does not take, N % 64 != 0),
+    each checked against the oracle and bitwise against its separate launch."""
+    shapes = [(256, 384), (64, 384), (640, 1088), (100, 192), (1024, 128)]  # (N, K)
+    data = [random_inputs(M, N, K, seed=7 * M + N + K) for (N, K) in shapes]
+    devs = [(dev(g), dev(s), dev(b)) for g, s, b in data]
+    outs = lib.grad_a_grouped(devs)
+    for (N, K), (g, s, b), d, o in zip(shapes, data, devs, outs):
+        gpu = host(o)
+        if N % 64 == 0:
+            sep = host(lib.grad_a_forced(*d, "wide16", rb=1, splits=1))
+        else:
+            sep = host(lib.grad_a(*d))
+        assert np.array_equal(gpu.view(np.uint32), sep.view(np.uint32)), (M, N, K)
+        ref, S = oracle.grad_a(g, s, b, M, N, K)
+        assert_within_bound(gpu, ref, S, f"grouped {M}x{N}x{K}")
+
+
+def test_grad_a_grouped_edges(lib):
+    g, s, b = random_inputs(40, 128, 256, seed=5)
+    d = (dev(g), dev(s), dev(b))
+    assert lib.grad_a_grouped([]) == []
+    # a single problem and a skinny M take the separate plans
+    one = lib.grad_a_grouped([d])
+    assert np.array_equal(host(one[0]).view(np.uint32), host(lib.grad_a_forced(*d, "wide16", rb=1, splits=1)).view(np.uint32))
+    gs, ss, bs = random_inputs(8, 128, 256, seed=6)
+    sk = lib.grad_a_grouped([(dev(gs), dev(ss), dev(bs))])
+    ref, S = oracle.grad_a(gs, ss, bs, 8, 128, 256)
+    assert_within_bound(host(sk[0]), ref, S, "grouped skinny")
+    with pytest.raises(ValueError):
+        lib.grad_a_grouped([d] * 9)
+
+
 def test_grad_a_wide_deterministic_and_rejects_ragged_n(lib):
     M, N, K = 700, 4096, 384
     g, s, b = random_inputs(M, N, K, seed=31)
