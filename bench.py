@@ -17,9 +17,11 @@ profiles/, reported only when that summary was taken on the current kernel
 source.  `cpu_baseline` is the fp64 CPU oracle timed on a bounded sample.
 `per_config` holds the four smaller workloads (tiny, attention projection,
 MLP pair, skinny sweep), timed with rotated input sets so they do not sit in
-the 256 MB Infinity Cache.
+the 256 MB Infinity Cache; `per_config_forward` the same layers' forward
+product and `per_config_rms_norm` the RMSNorm backward (algorithmic GB/s).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-configs]
+       python bench.py --forward-configs | --unfused-configs | --rmsnorm-configs   (side tables, one JSON line)
        python bench.py --copy-calibration   (1 GiB device copy, for counter scaling)
 """
 
@@ -282,6 +284,84 @@ def per_config_table(torch, nb, op="grad_a"):
     return out
 
 
+def rms_norm_alg_bytes(rows, H):
+    """x, dy read and dx written (fp32), gamma read and dgamma written, rms read."""
+    return 12 * rows * H + 8 * H + 4 * rows
+
+
+def per_config_rms_norm(torch, nb, rotate_bytes=512 << 20, target_s=0.02, trials=5):
+    """Per-shape timing of nf4_rms_norm_backward over rotated input sets (x, gamma, rms, dy, dx, dgamma);
+    HBM-bound, reported as algorithmic GB/s against the published HBM peak."""
+    import synth
+    out = {}
+    for i, (rows, H) in enumerate(synth.RMS_NORM_SHAPES):
+        per_set = rms_norm_alg_bytes(rows, H)
+        nsets = min(64, max(2, -(-rotate_bytes // per_set)))
+        gen = torch.Generator(device="cuda")
+        sets = []
+        for j in range(nsets):
+            gen.manual_seed(1000 * i + j)
+            x = torch.empty((rows, H), device="cuda").normal_(0.0, 1.0, generator=gen)
+            dy = torch.empty((rows, H), device="cuda").normal_(0.0, 1.0, generator=gen)
+            g = torch.empty((H,), device="cuda").uniform_(0.5, 1.5, generator=gen)
+            r = torch.empty((rows,), device="cuda").uniform_(0.9, 1.1, generator=gen)
+            sets.append((x, g, r, dy, torch.empty_like(x), torch.empty_like(g)))
+        torch.cuda.synchronize()
+        for j in range(5):
+            a = sets[j % nsets]
+            nb.rms_norm_backward(*a[:4], dx=a[4], dgamma=a[5])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        nb.rms_norm_backward(*sets[0][:4], dx=sets[0][4], dgamma=sets[0][5])
+        torch.cuda.synchronize()
+        one = max(time.perf_counter() - t0, 1e-6)
+        reps = int(min(max(target_s / one, 2 * nsets), 20000))
+        res = []
+        for _ in range(trials):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for k in range(reps):
+                a = sets[k % nsets]
+                nb.rms_norm_backward(*a[:4], dx=a[4], dgamma=a[5])
+            e1.record()
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1) * 1e-3 / reps)
+        del sets
+        torch.cuda.empty_cache()
+        res.sort()
+        med = res[len(res) // 2]
+        gb = rms_norm_alg_bytes(rows, H) / med / 1e9
+        out[f"rms_norm_{rows}x{H}"] = {"rows": rows, "H": H, "us": round(med * 1e6, 2),
+                                       "us_min": round(res[0] * 1e6, 2), "us_max": round(res[-1] * 1e6, 2),
+                                       "alg_bytes": rms_norm_alg_bytes(rows, H), "gbs": round(gb, 1),
+                                       "frac_of_hbm": round(gb / PEAK_HBM_GBS, 4), "rotated_input_sets": nsets}
+        log(f"[bench] rms_norm {rows}x{H}: {med * 1e6:.2f} us  {gb:.0f} GB/s")
+    return out
+
+
+def cpu_baseline_rms_norm(target_s=5.0):
+    """The fp64 RMSNorm-backward oracle on the 8192 x 3584 shape, repeated until about `target_s` seconds."""
+    import numpy as np
+    import synth
+    from oracle import rms_norm_oracle as ro
+    rows, H = 8192, 3584
+    t, n, reps = 0.0, 0, 0
+    while reps == 0 or t < target_s:
+        x, gamma, dy = synth.rms_norm_inputs(rows, H, seed=reps)
+        rms = np.sqrt(np.mean(x.astype(np.float64) ** 2, axis=1) + 1e-5).astype(np.float32)
+        t0 = time.perf_counter()
+        ro.rms_norm_backward(x, gamma, rms, dy)
+        t += time.perf_counter() - t0
+        n += rms_norm_alg_bytes(rows, H)
+        reps += 1
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(n / t / 1e9, 3), "unit": "GB/s", "cores": min(cores, int(os.environ.get("OMP_NUM_THREADS",
+                                                                                                    cores))),
+            "kind": "oracle", "seconds": round(t, 2),
+            "sample": f"{reps} x the 8192 x 3584 RMSNorm backward (numpy fp64), algorithmic bytes / oracle time"}
+
+
 def cpu_baseline(target_s=10.0, max_layers=8, op="grad_a"):
     """The fp64 oracle, as it stands, on a bounded sample of the full step: one layer's seven projections at
     3072 of the 8192 token rows each, repeated over further layers (fresh inputs) until about `target_s`
@@ -332,6 +412,8 @@ def main():
                     help="only the fused-against-unfused comparison table (one JSON line)")
     ap.add_argument("--forward-configs", action="store_true",
                     help="only the forward product's per-config table and its CPU oracle baseline (one JSON line)")
+    ap.add_argument("--rmsnorm-configs", action="store_true",
+                    help="only the RMSNorm backward's per-shape table and its CPU oracle baseline (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for scaling HBM byte counters) and exit")
     args = ap.parse_args()
@@ -348,6 +430,11 @@ def main():
 
     if args.unfused_configs:
         print(json.dumps({"per_config_unfused": per_config_unfused(torch, nb)}), flush=True)
+        return
+    if args.rmsnorm_configs:
+        rec = {"per_config_rms_norm": per_config_rms_norm(torch, nb),
+               "cpu_baseline_rms_norm": None if args.no_cpu else cpu_baseline_rms_norm()}
+        print(json.dumps(rec), flush=True)
         return
     if args.forward_configs:
         rec = {"per_config_forward": per_config_table(torch, nb, op="forward"),
@@ -428,6 +515,7 @@ def main():
 
     per_config = None if args.no_configs else per_config_table(torch, nb)
     per_config_fwd = None if args.no_configs else per_config_table(torch, nb, op="forward")
+    per_config_rms = None if args.no_configs else per_config_rms_norm(torch, nb)
     cpu = None if args.no_cpu else cpu_baseline()
 
     rec = {
@@ -458,6 +546,7 @@ def main():
         "cpu_baseline": cpu,
         "per_config": per_config,
         "per_config_forward": per_config_fwd,
+        "per_config_rms_norm": per_config_rms,
     }
     print(json.dumps(rec), flush=True)
 

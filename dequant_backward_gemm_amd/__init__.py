@@ -26,7 +26,7 @@ NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_HIP = 0, 1, 2, 3, 4
 
 EXPORTED_SYMBOLS = ("nf4_grad_a", "nf4_dequant", "nf4_pack", "nf4_status_string", "nf4_grad_a_plan",
                     "nf4_grad_a_forced", "nf4_release_workspaces", "nf4_forward", "nf4_forward_forced",
-                    "nf4_grad_a_grouped")
+                    "nf4_grad_a_grouped", "nf4_rms_norm_backward")
 GROUP_MAX = 8
 
 
@@ -65,6 +65,8 @@ def _load() -> ctypes.CDLL:
     lib.nf4_forward.restype = ctypes.c_int
     lib.nf4_forward_forced.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp]
     lib.nf4_forward_forced.restype = ctypes.c_int
+    lib.nf4_rms_norm_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp]
+    lib.nf4_rms_norm_backward.restype = ctypes.c_int
     lib.nf4_grad_a_grouped.argtypes = [ctypes.c_void_p, ci, i64, vp]
     lib.nf4_grad_a_grouped.restype = ctypes.c_int
     lib.nf4_release_workspaces.argtypes = []
@@ -203,6 +205,25 @@ def forward(a, scales, codes, out=None, stream=None, splits: int = 0):
         st = _lib.nf4_forward(_ptr(a), _ptr(scales), _ptr(codes), _ptr(out), M, N, K, _stream_handle(stream))
     _check(st, "nf4_forward")
     return out
+
+
+def rms_norm_backward(x, gamma, rms, dy, dx=None, dgamma=None, stream=None):
+    """(dx [rows, H], dgamma [H]) of RMSNorm; rms is the forward pass's sqrt(mean(x^2) + eps) per row."""
+    import torch
+    rows, H = x.shape
+    _require(x, torch.float32, (rows, H), "x")
+    _require(gamma, torch.float32, (H,), "gamma")
+    _require(rms, torch.float32, (rows,), "rms")
+    _require(dy, torch.float32, (rows, H), "dy")
+    if dx is None:
+        dx = torch.empty((rows, H), dtype=torch.float32, device=x.device)
+    if dgamma is None:
+        dgamma = torch.empty((H,), dtype=torch.float32, device=x.device)
+    _require(dx, torch.float32, (rows, H), "dx")
+    _require(dgamma, torch.float32, (H,), "dgamma")
+    _check(_lib.nf4_rms_norm_backward(_ptr(x), _ptr(gamma), _ptr(rms), _ptr(dy), _ptr(dx), _ptr(dgamma), rows, H,
+                                      _stream_handle(stream)), "nf4_rms_norm_backward")
+    return dx, dgamma
 
 
 def dequant(scales, codes, out=None, stream=None):

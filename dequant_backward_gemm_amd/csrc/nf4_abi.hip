@@ -130,6 +130,17 @@ int nf4_grad_a_grouped(const nf4_grad_a_problem* problems, int count, int64_t M,
   return from_hip(nf4::launch_grad_a_grouped(g, sc, cd, out, n, k, count, M, stream));
 }
 
+int nf4_rms_norm_backward(const float* x, const float* gamma, const float* rms, const float* dy, float* dx,
+                          float* dgamma, int64_t rows, int64_t H, hipStream_t stream) {
+  if (!dims_ok(rows, H) || !nf4::rms_norm_supported(rows, H)) return NF4_ERR_SHAPE;
+  if (gamma == nullptr || dgamma == nullptr) return NF4_ERR_NULL;
+  if (rows > 0 && (x == nullptr || rms == nullptr || dy == nullptr || dx == nullptr)) return NF4_ERR_NULL;
+  if (!aligned16(gamma) || !aligned16(dgamma) ||
+      (rows > 0 && (!aligned16(x) || !aligned16(rms) || !aligned16(dy) || !aligned16(dx))))
+    return NF4_ERR_ALIGN;
+  return from_hip(nf4::launch_rms_norm_backward(x, gamma, rms, dy, dx, dgamma, rows, H, stream));
+}
+
 int nf4_release_workspaces(void) { return from_hip(nf4::release_workspaces()); }
 
 const char* nf4_status_string(int status) {

@@ -83,6 +83,13 @@ hipError_t launch_grad_a_grouped(const float* const* grad_out, const float* cons
                                  const uint8_t* const* codes, float* const* grad_a, const int64_t* N,
                                  const int64_t* K, int count, int64_t M, hipStream_t stream);
 
+// RMSNorm backward (rms_norm_bwd.hip): H % 4 == 0, H <= 8192; uses
+// rms_norm_workspace_bytes(H) of the stream's workspace for dgamma partials.
+bool rms_norm_supported(int64_t rows, int64_t H);
+size_t rms_norm_workspace_bytes(int64_t H);
+hipError_t launch_rms_norm_backward(const float* x, const float* gamma, const float* rms, const float* dy, float* dx,
+                                    float* dgamma, int64_t rows, int64_t H, hipStream_t stream);
+
 // Unfused comparison path (kernel 6): the weights dequantised to fp16 once
 // into B fragments (unfused_bfrag_bytes(N, K) bytes), then the fragment-fed
 // wide kernel copying them into LDS instead of decoding.  Same preconditions

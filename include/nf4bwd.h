@@ -196,6 +196,30 @@ int nf4_forward_forced(const float* a, const float* scales, const uint8_t* codes
                        int64_t M, int64_t N, int64_t K, int splits, hipStream_t stream);
 
 /*
+ * nf4_rms_norm_backward -- the RMSNorm backward of the same training step
+ * (trueno-gpu 0.4.17, src/kernels/backward/rms_norm.rs, module documentation),
+ * fp32 throughout:
+ *
+ *   x      : const float [rows][H]   the forward pass's input
+ *   gamma  : const float [H]         the learned scale
+ *   rms    : const float [rows]      the forward pass's sqrt(mean(x^2) + eps)
+ *   dy     : const float [rows][H]   gradient of the output
+ *   dx     : float       [rows][H]   OVERWRITTEN:
+ *            dx_i = (gamma_i dy_i - x_i m / rms^2) / rms, m = mean_j(x_j dy_j gamma_j)
+ *   dgamma : float       [H]         OVERWRITTEN: sum over rows of dy_i x_i / rms
+ *
+ * dx is the exact derivative of the page's forward y_i = x_i / rms * gamma_i
+ * (the page's finite-difference prediction; its printed dx formula scales the
+ * correction term by gamma_i too, which agrees only at gamma = 1).  rms is used
+ * as stored.  Requires H % 4 == 0 and H <= 8192 (NF4_ERR_SHAPE otherwise);
+ * rows == 0 writes dgamma = 0.  Every pointer 16-byte aligned.  Bitwise
+ * deterministic (fixed summation orders, no atomics).  Uses 512 * H * 4 bytes
+ * of the stream's workspace for dgamma partials.
+ */
+int nf4_rms_norm_backward(const float* x, const float* gamma, const float* rms, const float* dy, float* dx,
+                          float* dgamma, int64_t rows, int64_t H, hipStream_t stream);
+
+/*
  * nf4_release_workspaces -- frees every cached split-N workspace.  It first
  * waits for all work on each device that holds one (hipDeviceSynchronize),
  * since the owning streams may no longer exist.  Host-blocking; not for use

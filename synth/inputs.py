@@ -98,6 +98,24 @@ def grad_out_normal(M: int, N: int, seed: int, std: float = 1.0) -> np.ndarray:
     return _rng(seed).normal(0.0, std, size=(M, N)).astype(np.float32)
 
 
+def rms_norm_inputs(rows: int, H: int, seed: int):
+    """RMSNorm backward inputs: x [rows][H] ~ N(0, 1), gamma [H] ~ U[0.5, 1.5), dy [rows][H] ~ N(0, 1), fp32.
+
+    Draw order x, gamma, dy from one stream.  (The per-row rms is the forward pass's, computed by whoever
+    consumes these.)
+    """
+    rng = _rng(seed)
+    x = rng.normal(0.0, 1.0, size=(rows, H)).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, size=(H,)).astype(np.float32)
+    dy = rng.normal(0.0, 1.0, size=(rows, H)).astype(np.float32)
+    return x, gamma, dy
+
+
+# RMSNorm backward workloads: the decoder's hidden size over the full step's 8192 tokens, the
+# attention-projection width, and the subject page's own (rows, hidden) test sizes.
+RMS_NORM_SHAPES = [(8192, 3584), (8192, 1536), (64, 32), (128, 16)]
+
+
 def tiny_inputs(seed: int = 0):
     """The tiny workload: random codes, scales U[0.01, 0.1), grad_out N(0, 1).
 
