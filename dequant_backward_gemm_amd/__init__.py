@@ -63,7 +63,7 @@ def _load() -> ctypes.CDLL:
     lib.nf4_grad_a_forced.restype = ctypes.c_int
     lib.nf4_forward.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     lib.nf4_forward.restype = ctypes.c_int
-    lib.nf4_forward_forced.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, vp]
+    lib.nf4_forward_forced.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, vp]
     lib.nf4_forward_forced.restype = ctypes.c_int
     lib.nf4_rms_norm_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp]
     lib.nf4_rms_norm_backward.restype = ctypes.c_int
@@ -187,8 +187,14 @@ def grad_a_forced(grad_out, scales, codes, kernel: str, rb: int = 2, splits: int
     return out
 
 
-def forward(a, scales, codes, out=None, stream=None, splits: int = 0):
-    """c[M, N] = a[M, K] . dequant(codes, scales)[N, K]^T (fp32); splits > 0 forces the K chunk count."""
+FORWARD_KERNELS = {"tile": 0, "stream": 1}
+
+
+def forward(a, scales, codes, out=None, stream=None, splits: int = 0, kernel: str = "auto"):
+    """c[M, N] = a[M, K] . dequant(codes, scales)[N, K]^T (fp32).
+
+    splits > 0 forces the K chunk count; kernel "tile" or "stream" forces the kernel ("auto" with a forced
+    split count takes the one nf4_forward would: streaming for M <= 16, tiles otherwise)."""
     import torch
     M, K = a.shape
     N = codes.shape[0]
@@ -198,9 +204,11 @@ def forward(a, scales, codes, out=None, stream=None, splits: int = 0):
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=a.device)
     _require(out, torch.float32, (M, N), "out")
-    if splits > 0:
-        st = _lib.nf4_forward_forced(_ptr(a), _ptr(scales), _ptr(codes), _ptr(out), M, N, K, splits,
-                                     _stream_handle(stream))
+    if splits > 0 or kernel != "auto":
+        if kernel == "auto":
+            kernel = "stream" if 1 <= M <= 16 else "tile"
+        st = _lib.nf4_forward_forced(_ptr(a), _ptr(scales), _ptr(codes), _ptr(out), M, N, K,
+                                     FORWARD_KERNELS[kernel], max(splits, 1), _stream_handle(stream))
     else:
         st = _lib.nf4_forward(_ptr(a), _ptr(scales), _ptr(codes), _ptr(out), M, N, K, _stream_handle(stream))
     _check(st, "nf4_forward")

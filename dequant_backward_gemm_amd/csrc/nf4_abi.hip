@@ -20,7 +20,7 @@ bool dims_ok(int64_t a, int64_t b) {
 int from_hip(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_HIP; }
 
 int forward_checked(const float* a, const float* scales, const uint8_t* codes, float* c, int64_t M, int64_t N,
-                    int64_t K, int splits, hipStream_t stream) {
+                    int64_t K, int kernel, int splits, hipStream_t stream) {
   if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N) || (K % 64) != 0 || (N % 8) != 0) return NF4_ERR_SHAPE;
   if (M == 0 || N == 0) return NF4_OK;
   if (c == nullptr) return NF4_ERR_NULL;
@@ -28,7 +28,8 @@ int forward_checked(const float* a, const float* scales, const uint8_t* codes, f
   if (!aligned16(c) || (K > 0 && (!aligned16(a) || !aligned16(scales) || !aligned16(codes)))) return NF4_ERR_ALIGN;
   if (K > 0 && !nf4::forward_supported(M, N, K)) return NF4_ERR_SHAPE;
   if (splits < 0 || splits > 4096) return NF4_ERR_SHAPE;
-  return from_hip(nf4::launch_nf4_forward(a, scales, codes, c, M, N, K, splits, stream));
+  if (kernel == nf4::kForwardStream && K > 0 && !nf4::forward_stream_supported(M, N, K)) return NF4_ERR_SHAPE;
+  return from_hip(nf4::launch_nf4_forward(a, scales, codes, c, M, N, K, kernel, splits, stream));
 }
 
 }  // namespace
@@ -91,13 +92,13 @@ int nf4_grad_a_plan(int64_t M, int64_t N, int64_t K, int* out5) {
 
 int nf4_forward(const float* a, const float* scales, const uint8_t* codes, float* c, int64_t M, int64_t N, int64_t K,
                 hipStream_t stream) {
-  return forward_checked(a, scales, codes, c, M, N, K, 0, stream);
+  return forward_checked(a, scales, codes, c, M, N, K, nf4::kForwardAuto, 0, stream);
 }
 
 int nf4_forward_forced(const float* a, const float* scales, const uint8_t* codes, float* c, int64_t M, int64_t N,
-                       int64_t K, int splits, hipStream_t stream) {
-  if (splits < 1) return NF4_ERR_SHAPE;
-  return forward_checked(a, scales, codes, c, M, N, K, splits, stream);
+                       int64_t K, int kernel, int splits, hipStream_t stream) {
+  if (splits < 1 || (kernel != nf4::kForwardTile && kernel != nf4::kForwardStream)) return NF4_ERR_SHAPE;
+  return forward_checked(a, scales, codes, c, M, N, K, kernel, splits, stream);
 }
 
 int nf4_grad_a_grouped(const nf4_grad_a_problem* problems, int count, int64_t M, hipStream_t stream) {

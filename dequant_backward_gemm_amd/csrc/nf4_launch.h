@@ -111,8 +111,17 @@ bool forward_supported(int64_t M, int64_t N, int64_t K);
 size_t forward_frag_bytes(int64_t M, int64_t K);
 hipError_t launch_forward(int grid, const float* a, void* frags, const float* scales, const uint32_t* codes,
                           float* dst, int M, int N, int K, int k_chunk, int tiles_m, int tiles_n, hipStream_t stream);
+// Streaming forward kernel for M <= 16 (nf4_forward_skinny.hip): 128-column
+// strips (16 per wave) x K chunks of whole 128-wide steps.
+bool forward_stream_supported(int64_t M, int64_t N, int64_t K);
+int forward_stream_strips(int64_t N);
+hipError_t launch_forward_stream(int grid, const float* a, const float* scales, const uint32_t* codes, float* dst,
+                                 int M, int N, int K, int k_chunk, int strips, hipStream_t stream);
+// kernel: -1 picks (streaming for M <= 16 where supported, else tiles), 0 tiles, 1 streaming;
+// splits <= 0 picks the K chunk count.
+constexpr int kForwardAuto = -1, kForwardTile = 0, kForwardStream = 1;
 hipError_t launch_nf4_forward(const float* a, const float* scales, const uint8_t* codes, float* c, int64_t M,
-                              int64_t N, int64_t K, int splits, hipStream_t stream);
+                              int64_t N, int64_t K, int kernel, int splits, hipStream_t stream);
 
 // Streaming kernel for M <= 16 (nf4_grad_a_skinny.hip): 128-column strips,
 // N-chunks of whole 32-row k-steps, two 8-wave workgroups per CU; needs

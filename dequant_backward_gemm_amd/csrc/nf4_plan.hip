@@ -311,9 +311,58 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
 // reduction is split into chunks of whole 64-wide stages (fp32 partials in the
 // stream's workspace, summed in chunk order by the reduce kernel).  splits <= 0
 // picks the count by the same cost model as the backward tiles.
+// Streaming forward (M <= 16): 128-column strips x K chunks of whole 128-wide
+// steps.  The chunk count comes from the same bandwidth model as the backward
+// streaming kernel (whole rounds of two workgroups per CU, partials and a
+// reduce launch per split); a split chunk keeps at least two steps.
+static hipError_t launch_nf4_forward_stream(const float* a, const float* scales, const uint8_t* codes, float* c,
+                                            int64_t M, int64_t N, int64_t K, int splits, hipStream_t stream) {
+  const int64_t strips = forward_stream_strips(N);
+  int64_t se = 1, chunk = K;
+  if (splits > 0) {
+    chunk = cdiv(cdiv(K, splits), 128) * 128;
+    se = cdiv(K, chunk);
+  } else {
+    const double bw = 5.0e12;
+    const double stream_bytes = (double)N * (double)K * (0.5 + 1.0 / 16.0) + 4.0 * (double)M * (double)(N + K);
+    const int64_t slots = 2 * kCUs;
+    double best = 1e30;
+    for (int64_t s = 1; s <= 64; ++s) {
+      const int64_t ch = cdiv(cdiv(K, s), 128) * 128;
+      const int64_t e = cdiv(K, ch);
+      if (e != s || (e > 1 && ch < 256)) continue;
+      const int64_t grid = strips * e;
+      const double rounds = (double)cdiv(grid, slots);
+      double t = stream_bytes / bw * (rounds * slots) / (double)grid + 3e-6 + (rounds - 1.0) * 1.5e-6;
+      if (e > 1) t += 2.0 * (double)e * (double)M * (double)N * 4.0 / bw + 4e-6;
+      if (t < best * 0.999) {
+        best = t;
+        se = e;
+        chunk = ch;
+      }
+    }
+  }
+  float* dst = c;
+  if (se > 1) {
+    hipError_t e = stream_workspace(stream, (size_t)se * (size_t)M * (size_t)N * sizeof(float),
+                                    reinterpret_cast<void**>(&dst));
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch_forward_stream((int)(strips * se), a, scales, reinterpret_cast<const uint32_t*>(codes), dst,
+                                       (int)M, (int)N, (int)K, (int)chunk, (int)strips, stream);
+  if (e != hipSuccess) return e;
+  if (se > 1) {
+    const int64_t n4 = M * N / 4;
+    e = launch_grad_a_reduce((int)std::min<int64_t>(cdiv(n4, 256), 8192), dst, c, n4, (int)se, stream);
+  }
+  return e;
+}
+
 hipError_t launch_nf4_forward(const float* a, const float* scales, const uint8_t* codes, float* c, int64_t M,
-                              int64_t N, int64_t K, int splits, hipStream_t stream) {
+                              int64_t N, int64_t K, int kernel, int splits, hipStream_t stream) {
   if (K == 0) return launch_fill_zero((int)std::min<int64_t>(cdiv(M * N / 4, 256), 4096), c, M * N / 4, stream);
+  if (kernel == kForwardStream || (kernel == kForwardAuto && forward_stream_supported(M, N, K)))
+    return launch_nf4_forward_stream(a, scales, codes, c, M, N, K, splits, stream);
   const int64_t tiles_m = cdiv(M, 512), tiles_n = cdiv(N, 128);
   const int64_t tiles = tiles_m * tiles_n;
   int64_t se = 1, chunk = K;

@@ -180,20 +180,27 @@ int nf4_grad_a_grouped(const nf4_grad_a_problem* problems, int count, int64_t M,
  *   fp16() round-to-nearest-even and w the fp32 dequantised weight.  Requires
  *   K % 64 == 0 and N % 8 == 0 (NF4_ERR_SHAPE otherwise), and a, codes below
  *   2 GiB.  M == 0 or N == 0 enqueues nothing; K == 0 writes zeros.  Bitwise
- *   deterministic for a given (M, N, K).  Uses the stream's workspace (see the
- *   shared rules) for an fp16 copy of `a` (2 * 16*ceil(M/16) * K bytes) and,
- *   when K is split, fp32 partials.
+ *   deterministic for a given (M, N, K).  1 <= M <= 16 runs a streaming
+ *   kernel (64-column strips of C, the weight read once); larger M runs
+ *   512 x 128 tiles.  Uses the stream's workspace (see the shared rules) for
+ *   an fp16 copy of `a` (tiles: 2 * 16*ceil(M/16) * K bytes) and, when K is
+ *   split, fp32 partials.
  */
 int nf4_forward(const float* a, const float* scales, const uint8_t* codes, float* c,
                 int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /*
- * nf4_forward_forced -- nf4_forward with the number of K chunks forced
- * (`splits` >= 1, rounded so that every chunk is a whole number of 64-wide
- * stages); for tests and tuning.  Same contract as nf4_forward.
+ * nf4_forward_forced -- nf4_forward with the kernel and the number of K
+ * chunks forced, for tests and tuning: kernel NF4_FORWARD_TILE (512 x 128
+ * tiles, any M) or NF4_FORWARD_STREAM (the streaming kernel nf4_forward picks
+ * for 1 <= M <= 16; NF4_ERR_SHAPE for other M); `splits` >= 1, rounded so that
+ * every chunk is a whole number of 64-wide blocks.  Same contract as
+ * nf4_forward otherwise (the streaming kernel needs no fp16 copy of `a`).
  */
+#define NF4_FORWARD_TILE 0
+#define NF4_FORWARD_STREAM 1
 int nf4_forward_forced(const float* a, const float* scales, const uint8_t* codes, float* c,
-                       int64_t M, int64_t N, int64_t K, int splits, hipStream_t stream);
+                       int64_t M, int64_t N, int64_t K, int kernel, int splits, hipStream_t stream);
 
 /*
  * nf4_rms_norm_backward -- the RMSNorm backward of the same training step
