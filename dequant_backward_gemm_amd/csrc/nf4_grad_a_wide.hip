@@ -163,12 +163,15 @@ __global__ __launch_bounds__(512) void dequant_bfrag_kernel(const float* __restr
   }
 }
 
-// One workgroup's tile of the wide kernel; `logical` is its tile index in the
-// (k-tile fastest, then m-tile, then N-chunk) order.
+// One workgroup's tile of the wide kernel over the reduction rows [nb, ne)
+// (whole 64-row stages): tile `tile` in (k-tile fastest, then m-tile) order.
+// Output element (row, col) of the tile goes to dst[(row - row0) * ld + col -
+// col0] (rows < M and columns < K only).
 template <int WC, int AF, bool BCOPY>
 __device__ __forceinline__ void wide_tile(const void* __restrict__ Gv, const float* __restrict__ S,
-                                          const uint32_t* __restrict__ C32, float* __restrict__ out, int M, int N,
-                                          int K, int n_chunk, int tiles_m, int tiles_k, int logical) {
+                                          const uint32_t* __restrict__ C32, int M, int N, int K, int tiles_k,
+                                          int tile, int nb, int ne, float* __restrict__ dst, int ld, int row0,
+                                          int col0) {
   // AF == 0: Gv is grad_out (fp32 [M][N]); AF > 0: Gv holds the fp16 A
   // fragments of grad_out_frag_kernel and AF k-steps of them are in flight.
   // BCOPY: C32 holds the fp16 B fragments of dequant_bfrag_kernel, which are
@@ -187,13 +190,9 @@ __device__ __forceinline__ void wide_tile(const void* __restrict__ Gv, const flo
   const int ci = lane & 15, q = lane >> 4;  // MFMA lane: row / column index, quarter
   const int wr = wave % WR, wc = wave / WR;
 
-  const int kt = logical % tiles_k;
-  const int rest = logical / tiles_k;
-  const int mt = rest % tiles_m;
-  const int split = rest / tiles_m;
+  const int kt = tile % tiles_k;
+  const int mt = tile / tiles_k;
   const int m0 = mt * BM, k0 = kt * BK;
-  const int nb = split * n_chunk;
-  const int ne = min(N, nb + n_chunk);
   const int nst = (ne - nb) >> 6;
 
   const __amdgpu_buffer_rsrc_t rc =
@@ -529,7 +528,6 @@ __device__ __forceinline__ void wide_tile(const void* __restrict__ Gv, const flo
   if (st < nst) stage(st, std::integral_constant<uint32_t, 0>{});
 
   // 16x16 accumulator layout: lane (ci, q), register r -> row 4*q + r, column ci.
-  float* __restrict__ dst = out + (size_t)split * (size_t)M * (size_t)K;
   const int col = k0 + 128 * wc + 8 * ci;
   if (col < K) {
 #pragma unroll
@@ -540,7 +538,7 @@ __device__ __forceinline__ void wide_tile(const void* __restrict__ Gv, const flo
         if (row < M) {
           const floatx4 lo = {acc[rb][0][r], acc[rb][1][r], acc[rb][2][r], acc[rb][3][r]};
           const floatx4 hi = {acc[rb][4][r], acc[rb][5][r], acc[rb][6][r], acc[rb][7][r]};
-          floatx4* o = reinterpret_cast<floatx4*>(dst + (size_t)row * (size_t)K + col);
+          floatx4* o = reinterpret_cast<floatx4*>(dst + (size_t)(row - row0) * (size_t)ld + (col - col0));
           o[0] = lo;
           o[1] = hi;
         }
@@ -549,11 +547,99 @@ __device__ __forceinline__ void wide_tile(const void* __restrict__ Gv, const flo
   }
 }
 
+// One tile over one N-chunk per workgroup; the chunk index is the slowest
+// part of the logical index and selects the partial-sum matrix it writes.
 template <int WC, int AF, bool BCOPY = false>
 __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
     const void* __restrict__ Gv, const float* __restrict__ S, const uint32_t* __restrict__ C32,
     float* __restrict__ out, int M, int N, int K, int n_chunk, int tiles_m, int tiles_k) {
-  wide_tile<WC, AF, BCOPY>(Gv, S, C32, out, M, N, K, n_chunk, tiles_m, tiles_k, xcd_remap(blockIdx.x, gridDim.x));
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int tiles = tiles_m * tiles_k;
+  const int split = logical / tiles;
+  const int nb = split * n_chunk;
+  wide_tile<WC, AF, BCOPY>(Gv, S, C32, M, N, K, tiles_k, logical % tiles, nb, min(N, nb + n_chunk),
+                           out + (size_t)split * (size_t)M * (size_t)K, K, 0, 0);
+}
+
+// Stream-K launch of the fragment-fed kernel.  The (tile, stage) iterations of
+// the whole product, tiles in (k-tile fastest, then m-tile) order and stages in
+// reduction order, are cut into `gridDim.x` equal contiguous ranges, one per
+// workgroup, so every CU gets the same amount of work whatever the tile count.
+// A workgroup walks its range tile by tile: a tile it covers whole is written
+// to grad_A directly; a piece of a tile split between workgroups (only a
+// range's first and last piece can be one) goes to the workgroup's partial
+// slot 2w (first piece) or 2w + 1 (last piece), BM x BK fp32, and
+// streamk_fixup_kernel adds a split tile's pieces in workgroup order, which is
+// reduction order.
+__device__ __forceinline__ int64_t streamk_begin(int w, int G, int64_t total) { return (int64_t)w * total / G; }
+
+__global__ __launch_bounds__(512, 1) void grad_a_wide_streamk_kernel(const void* __restrict__ frags,
+                                                                     const float* __restrict__ S,
+                                                                     const uint32_t* __restrict__ C32,
+                                                                     float* __restrict__ out,
+                                                                     float* __restrict__ slots, int M, int N, int K,
+                                                                     int tiles_m, int tiles_k) {
+  using Cfg = WideCfg<1>;
+  const int G = gridDim.x;
+  const int w = xcd_remap(blockIdx.x, G);
+  const int spt = N / 64;  // stages per tile
+  const int64_t total = (int64_t)tiles_m * tiles_k * spt;
+  const int64_t it1 = streamk_begin(w + 1, G, total);
+  int64_t it = streamk_begin(w, G, total);
+  const int64_t it0 = it;
+  while (it < it1) {
+    const int tile = (int)(it / spt);
+    const int st0 = (int)(it % spt);
+    const int st1 = (int)std::min<int64_t>((int64_t)spt, (int64_t)st0 + (it1 - it));
+    const bool whole = st0 == 0 && st1 == spt;
+    float* dst = whole ? out : slots + (size_t)(2 * w + (it == it0 ? 0 : 1)) * (size_t)(Cfg::BM * Cfg::BK);
+    wide_tile<1, WIDE_FRAG_DEPTH, false>(frags, S, C32, M, N, K, tiles_k, tile, 64 * st0, 64 * st1, dst,
+                                         whole ? K : Cfg::BK, whole ? 0 : (tile / tiles_k) * Cfg::BM,
+                                         whole ? 0 : (tile % tiles_k) * Cfg::BK);
+    it += st1 - st0;
+    __syncthreads();  // the next piece's prologue rewrites the LDS buffers
+  }
+}
+
+// Sums the pieces of every split tile (one workgroup per tile; tiles covered
+// by a single workgroup return at once): workgroups w_a .. w_b with a
+// non-empty share hold the tile's pieces in reduction order, each in slot 2w
+// if the piece starts its share, else 2w + 1.
+__global__ __launch_bounds__(512) void streamk_fixup_kernel(const float* __restrict__ slots, float* __restrict__ out,
+                                                            int M, int N, int K, int tiles_k, int G) {
+  using Cfg = WideCfg<1>;
+  const int tile = blockIdx.x;
+  const int spt = N / 64;
+  const int64_t total = (int64_t)gridDim.x * spt;
+  const int64_t t0 = (int64_t)tile * spt, t1 = t0 + spt;
+  // workgroup holding iteration i: the largest w with streamk_begin(w) <= i
+  auto owner = [&](int64_t i) {
+    int w = (int)((i * G) / total);
+    while (w + 1 < G && streamk_begin(w + 1, G, total) <= i) ++w;
+    while (w > 0 && streamk_begin(w, G, total) > i) --w;
+    return w;
+  };
+  const int wa = owner(t0), wb = owner(t1 - 1);
+  if (wa == wb) return;
+  const int m0 = (tile / tiles_k) * Cfg::BM, k0 = (tile % tiles_k) * Cfg::BK;
+  constexpr int kVec = Cfg::BM * Cfg::BK / 4;  // float4 elements per slot
+  for (int e = threadIdx.x; e < kVec; e += 512) {
+    floatx4 sum = {0.f, 0.f, 0.f, 0.f};
+    bool first = true;
+    for (int w = wa; w <= wb; ++w) {
+      const int64_t b = streamk_begin(w, G, total);
+      if (streamk_begin(w + 1, G, total) == b) continue;  // an empty share (more shares than iterations)
+      const int slot = 2 * w + (b >= t0 ? 0 : 1);
+      const floatx4 v = reinterpret_cast<const floatx4*>(slots + (size_t)slot * (size_t)(Cfg::BM * Cfg::BK))[e];
+      if (first)
+        sum = v;
+      else
+        sum += v;
+      first = false;
+    }
+    const int row = m0 + (4 * e) / Cfg::BK, col = k0 + (4 * e) % Cfg::BK;
+    if (row < M && col < K) *reinterpret_cast<floatx4*>(out + (size_t)row * (size_t)K + col) = sum;
+  }
 }
 
 // Grouped launch: the tiles of up to kWideGroupMax problems sharing M (each
@@ -586,7 +672,7 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_grouped_kernel(WideGroup g
       tiles_k = g.p[j].tiles_k;
       begin = g.p[j].tile_begin;
     }
-  wide_tile<1, WIDE_FRAG_DEPTH, false>(frags, scales, codes, out, g.M, N, K, N, g.tiles_m, tiles_k, tile - begin);
+  wide_tile<1, WIDE_FRAG_DEPTH, false>(frags, scales, codes, g.M, N, K, tiles_k, tile - begin, 0, N, out, K, 0, 0);
 }
 
 bool wide_kernel_supported(int64_t M, int64_t N, int64_t K) {
@@ -643,6 +729,22 @@ hipError_t launch_frag_pass(const float* src, void* frags, int rows, int cols, b
   else
     hipLaunchKernelGGL(grad_out_frag_kernel<false>, dim3(pgrid), dim3(256), 0, stream, src, static_cast<u32x4*>(frags),
                        rows, cols, total);
+  return hipGetLastError();
+}
+
+size_t streamk_slot_bytes(int grid) { return (size_t)grid * 2 * WideCfg<1>::BM * WideCfg<1>::BK * sizeof(float); }
+
+hipError_t launch_grad_a_wide_streamk(int grid, const float* grad_out, void* frags, float* slots, const float* scales,
+                                      const uint32_t* codes, float* out, int M, int N, int K, hipStream_t stream) {
+  hipError_t e = launch_frag_pass(grad_out, frags, M, N, /*natural=*/false, stream);
+  if (e != hipSuccess) return e;
+  const int tiles_m = (M + WideCfg<1>::BM - 1) / WideCfg<1>::BM, tiles_k = (K + WideCfg<1>::BK - 1) / WideCfg<1>::BK;
+  hipLaunchKernelGGL(grad_a_wide_streamk_kernel, dim3(grid), dim3(512), 0, stream, frags, scales, codes, out, slots, M,
+                     N, K, tiles_m, tiles_k);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(streamk_fixup_kernel, dim3(tiles_m * tiles_k), dim3(512), 0, stream, slots, out, M, N, K, tiles_k,
+                     grid);
   return hipGetLastError();
 }
 

@@ -24,11 +24,12 @@ struct GradAPlan {
   int kernel;    // 0 = tile (BM = 128 * rb), 1 = skinny (M <= 16), 2 = zero-fill (N == 0),
                  // 3 = wide (8 waves, tile (512 / rb) x (128 * rb)), 4 = stream (M <= 16),
                  // 5 = wide fed by fp16 A fragments from a conversion pass (tile 512 x 128),
-                 // 6 = unfused comparison path (fp16 weight pass, then a fragment-copy GEMM)
+                 // 6 = unfused comparison path (fp16 weight pass, then a fragment-copy GEMM),
+                 // 7 = kernel 5's tiles launched stream-K (equal shares of all tile stages)
   int rb;        // tile: 32-row blocks per wave; wide: 128-column groups
   int splits;    // number of N-chunks (1 = no workspace, no reduce launch)
   int n_chunk;   // rows of N per chunk
-  int grid;      // workgroups of the main kernel
+  int grid;      // workgroups of the main kernel (kernel 7: the number of shares)
 };
 GradAPlan plan_grad_a(int64_t M, int64_t N, int64_t K);
 
@@ -59,6 +60,13 @@ hipError_t launch_grad_a_wide(int wc, int grid, const float* grad_out, const flo
 // workspace of wide_frag_bytes(M, N) bytes, then the wide kernel (tile 512 x
 // 128) reads them.  Same preconditions as the wide kernel.
 size_t wide_frag_bytes(int64_t M, int64_t N);
+// Stream-K launch of the fragment-fed wide kernel (kernel 7): `grid`
+// workgroups share the product's (tile, stage) iterations equally; pieces of
+// tiles split between workgroups go through streamk_slot_bytes(grid) bytes of
+// partial slots and a fixup kernel that adds them in reduction order.
+size_t streamk_slot_bytes(int grid);
+hipError_t launch_grad_a_wide_streamk(int grid, const float* grad_out, void* frags, float* slots, const float* scales,
+                                      const uint32_t* codes, float* out, int M, int N, int K, hipStream_t stream);
 hipError_t launch_grad_a_wide_frag(int grid, const float* grad_out, void* frags, const float* scales,
                                    const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,
                                    int tiles_k, hipStream_t stream);

@@ -186,6 +186,11 @@ GradAPlan plan_grad_a(int64_t M, int64_t N, int64_t K) {
     consider(3, 1, wide_tile_rows(1), wide_tile_cols(1), 1, 0.28, 0.0);
     consider(3, 2, wide_tile_rows(2), wide_tile_cols(2), 1, 0.11, 0.0);
     consider(5, 1, wide_tile_rows(1), wide_tile_cols(1), 1, 0.40, 6.0 * (double)M * (double)N / 5.5e12 + 2e-6);
+    // (Kernel 7, the same tiles launched stream-K, is not considered: despite
+    // the even load it measured 3-32% slower than the plans above on every
+    // large and mid-size shape -- most likely because, with the shares'
+    // starting stages scattered, the workgroups of an XCD no longer walk one
+    // m-tile's grad_out fragments in step and stop sharing them in L2.)
   }
   return p;
 }
@@ -230,6 +235,14 @@ bool make_plan(int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, 
     p.n_chunk = (int)chunk;
     p.splits = (int)cdiv(N, chunk);
     p.grid = (int)(cdiv(M, wide_tile_rows(1)) * cdiv(K, wide_tile_cols(1)) * p.splits);
+  } else if (kernel == 7) {
+    // `splits` is the number of stream-K shares (workgroups)
+    if (!wide_kernel_supported(M, N, K)) return false;
+    p.kernel = 7;
+    p.rb = 1;
+    p.splits = 1;
+    p.n_chunk = (int)N;
+    p.grid = splits;
   } else if (kernel == 3) {
     if ((rb != 1 && rb != 2) || !wide_kernel_supported(M, N, K)) return false;
     const int64_t chunk = cdiv(cdiv(N, splits), 64) * 64;
@@ -262,9 +275,9 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
     // workspace: split partials, then (fragment-fed wide kernel) the fp16 A fragments
     const size_t part = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)K * sizeof(float) : 0;
     const size_t part_al = (part + 255) & ~(size_t)255;
-    const size_t frag = (p.kernel == 5 || p.kernel == 6) ? wide_frag_bytes(M, N) : 0;
+    const size_t frag = (p.kernel == 5 || p.kernel == 6 || p.kernel == 7) ? wide_frag_bytes(M, N) : 0;
     const size_t frag_al = (frag + 255) & ~(size_t)255;
-    const size_t bfrag = p.kernel == 6 ? unfused_bfrag_bytes(N, K) : 0;
+    const size_t bfrag = p.kernel == 6 ? unfused_bfrag_bytes(N, K) : p.kernel == 7 ? streamk_slot_bytes(p.grid) : 0;
     if (part + frag + bfrag > 0) {
       char* base = nullptr;
       hipError_t e = stream_workspace(stream, part_al + frag_al + bfrag, reinterpret_cast<void**>(&base));
@@ -285,6 +298,9 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
   } else if (p.kernel == 6) {
     e = launch_grad_a_unfused(p.grid, grad_out, frags, bfrags, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
                               (int)cdiv(M, wide_tile_rows(1)), (int)cdiv(K, wide_tile_cols(1)), stream);
+  } else if (p.kernel == 7) {
+    e = launch_grad_a_wide_streamk(p.grid, grad_out, frags, static_cast<float*>(bfrags), scales, c32, dst, (int)M,
+                                   (int)N, (int)K, stream);
   } else if (p.kernel == 5) {
     e = launch_grad_a_wide_frag(p.grid, grad_out, frags, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
                                 (int)cdiv(M, wide_tile_rows(1)), (int)cdiv(K, wide_tile_cols(1)), stream);

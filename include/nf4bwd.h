@@ -110,10 +110,11 @@ const char* nf4_status_string(int status);
  * uses for a shape (no device work).  out5 receives, in order: kernel
  * (0 = tiled, 1 = skinny M <= 16, 2 = zero fill for N == 0, 3 = wide tiled,
  * 4 = streaming M <= 16 with 128-column strips, 5 = wide tiled fed by an fp16
- * A-fragment conversion pass of grad_out), the kernel's tile parameter
+ * A-fragment conversion pass of grad_out, 7 = kernel 5's tiles launched
+ * stream-K), the kernel's tile parameter
  * (tiled: 32-row blocks per wave; wide: column groups of 128, the tile being
  * 512 x 128 or 256 x 256; 0 for the others), number of N-chunks
- * (1 = no workspace), rows per N-chunk, workgroups of the main launch.
+ * (1 = no split partials), rows per N-chunk, workgroups of the main launch.
  * Returns NF4_ERR_SHAPE / NF4_ERR_NULL like nf4_grad_a.
  */
 int nf4_grad_a_plan(int64_t M, int64_t N, int64_t K, int* out5);
@@ -130,8 +131,12 @@ int nf4_grad_a_plan(int64_t M, int64_t N, int64_t K, int* out5);
  * unfused comparison path: the weights dequantised to fp16 by a separate pass
  * (2 * N * 128*ceil(K/128) bytes of workspace), then the kernel-5 GEMM
  * reading them instead of decoding (same requirements, bitwise the same
- * result as kernel 5);
- * `splits` = requested number of N-chunks
+ * result as kernel 5), kernel 7 = kernel 5's tiles launched stream-K: `splits`
+ * workgroups each take an equal contiguous share of all (tile, 64-row stage)
+ * iterations, a tile split between workgroups is summed from their fp32
+ * pieces in reduction order by a fixup kernel (2 * splits * 512 * 128 * 4
+ * bytes of workspace besides the fragments; `rb` ignored);
+ * otherwise `splits` = requested number of N-chunks
  * (rounded so that every chunk but the last is a whole number of stages).
  * Same contract and results-to-bound as nf4_grad_a; NF4_ERR_SHAPE if the
  * forced plan does not fit the shape.

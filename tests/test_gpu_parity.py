@@ -195,6 +195,36 @@ def test_grad_a_wide16_matches_wide_bitwise(lib):
         lib.grad_a_forced(dev(g[:, :2000]), sd[:2000], bd[:2000], "wide16", rb=1)
 
 
+@pytest.mark.parametrize("shares", [1, 3, 7, 64, 256])
+@pytest.mark.parametrize("M,N,K", [(17, 64, 64), (200, 384, 768), (513, 640, 320), (600, 1024, 448),
+                                   (1030, 256, 1088), (31, 128, 128)])
+def test_grad_a_streamk_ragged(lib, shares, M, N, K):
+    """Stream-K launch of the wide16 tiles: shares from 1 (one workgroup walks every tile) to more shares
+    than (tile, stage) iterations (empty shares), tiles split between two or more workgroups and summed
+    by the fixup, ragged M and K."""
+    g, s, b = random_inputs(M, N, K, seed=M + 3 * N + K + 11 * shares)
+    check_grad_a(lib, g, s, b, M, N, K, kernel="wide16sk", rb=1, splits=shares,
+                 what=f"wide16sk G{shares} {M}x{N}x{K}")
+
+
+def test_grad_a_streamk_unsplit_tiles_match_wide16_bitwise(lib):
+    """With one share, or shares that hold whole tiles only, no tile is split: every tile runs the wide16
+    body over its full reduction and the results equal the plain launch bit for bit; split tiles are
+    repeatable bit for bit."""
+    M, N, K = 600, 1024, 512  # 2 x 4 tiles of 16 stages
+    g, s, b = random_inputs(M, N, K, seed=41)
+    gd, sd, bd = dev(g), dev(s), dev(b)
+    base = host(lib.grad_a_forced(gd, sd, bd, "wide16", rb=1, splits=1))
+    for shares in (1, 2, 4, 8):
+        r = host(lib.grad_a_forced(gd, sd, bd, "wide16sk", rb=1, splits=shares))
+        assert np.array_equal(r.view(np.uint32), base.view(np.uint32)), shares
+    r1 = host(lib.grad_a_forced(gd, sd, bd, "wide16sk", rb=1, splits=5))
+    r2 = host(lib.grad_a_forced(gd, sd, bd, "wide16sk", rb=1, splits=5))
+    assert np.array_equal(r1.view(np.uint32), r2.view(np.uint32))
+    ref, S = oracle.grad_a(g, s, b, M, N, K)
+    assert_within_bound(r1, ref, S, "wide16sk G5")
+
+
 @pytest.mark.parametrize("splits", [1, 3])
 @pytest.mark.parametrize("M,N,K", [(17, 64, 64), (200, 384, 768), (513, 640, 320), (1030, 256, 1088)])
 def test_grad_a_unfused_matches_fused_bitwise(lib, splits, M, N, K):
