@@ -22,6 +22,7 @@ product and `per_config_rms_norm` the RMSNorm backward (algorithmic GB/s).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-configs]
        python bench.py --forward-configs | --unfused-configs | --rmsnorm-configs   (side tables, one JSON line)
+       python bench.py --one M,N,K [--steps K] [--warmup W]   (one shape, for counter collection)
        python bench.py --copy-calibration   (1 GiB device copy, for counter scaling)
 """
 
@@ -414,6 +415,9 @@ def main():
                     help="only the forward product's per-config table and its CPU oracle baseline (one JSON line)")
     ap.add_argument("--rmsnorm-configs", action="store_true",
                     help="only the RMSNorm backward's per-shape table and its CPU oracle baseline (one JSON line)")
+    ap.add_argument("--one", type=str, default=None, metavar="M,N,K",
+                    help="only run nf4_grad_a on one shape (packed N(0, 0.02) weights, grad_out N(0, 1e-2)) "
+                         "--steps times after --warmup calls, for counter collection; prints one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for scaling HBM byte counters) and exit")
     args = ap.parse_args()
@@ -428,6 +432,28 @@ def main():
         return
     import dequant_backward_gemm_amd as nb
 
+    if args.one:
+        M, N, K = (int(v) for v in args.one.split(","))
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(0)
+        w = torch.empty((N, K), device="cuda").normal_(0.0, 0.02, generator=gen)
+        s, c = nb.pack(w)
+        del w
+        g = torch.empty((M, N), device="cuda").normal_(0.0, 1e-2, generator=gen)
+        o = torch.empty((M, K), device="cuda")
+        for _ in range(args.warmup):
+            nb.grad_a(g, s, c, out=o)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            nb.grad_a(g, s, c, out=o)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / max(args.steps, 1)
+        print(json.dumps({"shape": [M, N, K], "plan": nb.grad_a_plan(M, N, K), "us_per_call": round(us, 2),
+                          "tflops": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 2)}), flush=True)
+        return
     if args.unfused_configs:
         print(json.dumps({"per_config_unfused": per_config_unfused(torch, nb)}), flush=True)
         return
