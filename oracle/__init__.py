@@ -10,6 +10,7 @@ from oracle.nf4_oracle import (  # noqa: F401
     NF4_LEVELS,
     codebook_from_quantiles,
     dequant,
+    dequant_columns,
     forward,
     grad_a,
     grad_a_bruteforce,

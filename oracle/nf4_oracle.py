@@ -121,13 +121,27 @@ def dequant(scales: np.ndarray, code_bytes: np.ndarray, N: int, K: int) -> np.nd
     return (np.repeat(s, NF4_BLOCK, axis=1) * q).astype(np.float32)
 
 
+def dequant_columns(scales: np.ndarray, code_bytes: np.ndarray, N: int, K: int, cols: np.ndarray) -> np.ndarray:
+    """fp32 [N][len(cols)]: the columns k in `cols` of dequant(), from the same definition -- code(n, k) is
+    the low nibble of byte k/2 of row n for even k, the high nibble for odd k; w = fl32(scale[n][k/64] *
+    level[code]) -- without unpacking the other columns (for weights too large to dequantise whole)."""
+    c = np.asarray(cols, dtype=np.int64)
+    b = np.asarray(code_bytes, dtype=np.uint8).reshape(N, K // 2)[:, c // 2]
+    codes = np.where((c % 2) == 0, b & 0x0F, b >> 4)
+    s = np.asarray(scales, dtype=np.float32).reshape(N, K // NF4_BLOCK)[:, c // NF4_BLOCK].astype(np.float64)
+    return (s * NF4_LEVELS.astype(np.float64)[codes]).astype(np.float32)
+
+
 def grad_a(grad_out: np.ndarray, scales: np.ndarray, code_bytes: np.ndarray, M: int, N: int, K: int,
-           rows: np.ndarray | None = None, with_bound: bool = True):
-    """fp64 grad_A and its bound scale S for the given (or all) rows.
+           rows: np.ndarray | None = None, with_bound: bool = True, cols: np.ndarray | None = None):
+    """fp64 grad_A and its bound scale S for the given (or all) rows and columns.
 
     ref[m][k] = sum_n g[m][n] * w[n][k];  S[m][k] = sum_n |g[m][n] * w[n][k]|.
     """
-    w = dequant(scales, code_bytes, N, K).astype(np.float64)
+    if cols is None:
+        w = dequant(scales, code_bytes, N, K).astype(np.float64)
+    else:
+        w = dequant_columns(scales, code_bytes, N, K, cols).astype(np.float64)
     g = np.asarray(grad_out, dtype=np.float32).reshape(M, N)
     if rows is not None:
         g = g[np.asarray(rows)]

@@ -363,6 +363,57 @@ def test_grad_a_full_step_shapes_sampled_rows(lib, proj):
     assert_within_bound(gpu[rows], ref, S, f"full_step {proj}")
 
 
+# ------------------------------------------------- maximum sizes: operands of 2 GiB and more
+
+def test_grad_a_skinny_with_codes_of_2_gib(lib):
+    """M <= 16 with a 2 GiB code array (N * K / 2 = 2^31 bytes, past the streaming kernel's 32-bit byte
+    offsets): the planner falls back to the skinny kernel, whose offsets are 64-bit.  All 16 rows on 48
+    sampled columns (column-sampled oracle)."""
+    M, N, K = 16, 65536, 65536
+    plan = lib.grad_a_plan(M, N, K)
+    assert plan["kernel"] == "skinny"
+    rng = np.random.default_rng(77)
+    b = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    s = synth.random_scales_uniform(N, K, seed=78)
+    g = synth.grad_out_normal(M, N, seed=79)
+    gpu = host(lib.grad_a(dev(g), dev(s), dev(b)))
+    cols = np.unique(np.concatenate([[0, 1, K - 2, K - 1], rng.integers(0, K, size=44)]))
+    ref, S = oracle.grad_a(g, s, b, M, N, K, cols=cols)
+    assert_within_bound(gpu[:, cols], ref, S, "skinny 2 GiB codes")
+    assert np.all(np.isfinite(gpu))
+
+
+def test_grad_a_large_m_with_grad_out_of_2_gib(lib):
+    """M > 16 with a 2 GiB grad_out (M * N * 4 = 2^31 bytes, past the wide kernels' 32-bit offsets): the
+    tile kernel's general path.  grad_out is drawn on the device (seeded torch generator); 12 sampled
+    rows are copied back for the oracle."""
+    M, N, K = 8192, 65536, 256
+    plan = lib.grad_a_plan(M, N, K)
+    assert plan["kernel"] == "tile"
+    b = synth.random_code_bytes(N, K, seed=81)
+    s = synth.random_scales_uniform(N, K, seed=82)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(83)
+    gd = torch.empty((M, N), device="cuda").normal_(0.0, 1e-2, generator=gen)
+    gpu = lib.grad_a(gd, dev(s), dev(b))
+    rows = np.array([0, 1, 4095, 4096, 6000, M - 2, M - 1, 17, 512, 1023, 3000, 7777])
+    g_rows = host(gd[torch.from_numpy(rows).cuda()])
+    gpu_rows = host(gpu)[rows]
+    del gd, gpu
+    ref, S = oracle.grad_a(g_rows, s, b, len(rows), N, K)
+    assert_within_bound(gpu_rows, ref, S, "tile 2 GiB grad_out")
+
+
+def test_forward_rejects_codes_of_2_gib(lib):
+    """The forward kernels take codes below 2 GiB only: NF4_ERR_SHAPE before any launch."""
+    N, K = 65536, 65536
+    b = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
+    s = torch.ones((N, K // 64), dtype=torch.float32, device="cuda")
+    a = torch.ones((1, K), dtype=torch.float32, device="cuda")
+    with pytest.raises(lib.Nf4Error):
+        lib.forward(a, s, b)
+
+
 # ------------------------------------------------- metamorphic / exact checks
 
 def test_grad_a_deterministic(lib):

@@ -91,6 +91,29 @@ def test_dequant_scale_index_probe():
             assert w[n, k] == 2.0 ** (n * 4 + k // 64 - 8)
 
 
+def test_dequant_columns_probes_and_agreement():
+    """Column-sampled dequant: the nibble-order and scale-index probes on odd and even sampled columns, and
+    bitwise agreement with the full dequant's columns (and grad_a's) on random inputs."""
+    N, K = 4, 256
+    s = np.array([[2.0 ** (n * 4 + kb - 8) for kb in range(4)] for n in range(N)], dtype=np.float32)
+    b = np.full((N, K // 2), 0x7F, dtype=np.uint8)  # even k -> code 15, odd k -> code 7
+    cols = np.array([0, 1, 63, 64, 130, 255])
+    w = oracle.dequant_columns(s, b, N, K, cols)
+    for n in range(N):
+        for j, k in enumerate(cols):
+            assert w[n, j] == (2.0 ** (n * 4 + k // 64 - 8) if k % 2 == 0 else 0.0)
+    N, K = 29, 448
+    b = synth.random_code_bytes(N, K, seed=21)
+    s = synth.random_scales_uniform(N, K, seed=22)
+    cols = np.random.default_rng(23).choice(K, size=40, replace=False)
+    assert np.array_equal(oracle.dequant_columns(s, b, N, K, cols).view(np.uint32),
+                          oracle.dequant(s, b, N, K)[:, cols].view(np.uint32))
+    g = synth.grad_out_normal(5, N, seed=24)
+    ref, S = oracle.grad_a(g, s, b, 5, N, K)
+    ref_c, S_c = oracle.grad_a(g, s, b, 5, N, K, cols=cols)
+    assert np.array_equal(ref_c, ref[:, cols]) and np.array_equal(S_c, S[:, cols])
+
+
 def test_dequant_is_one_fp32_multiply():
     """Bit-identical to an IEEE fp32 multiply done in float32 arithmetic."""
     N, K = 37, 320
