@@ -167,6 +167,26 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "copies": 3}), flush=True)
 
 
+def copy_bandwidth(torch, trials=5):
+    """Measured device-copy bandwidth (1 GiB read + 1 GiB written per copy), for information only."""
+    n = 256 << 20
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, 8.0 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del a, b
+    torch.cuda.empty_cache()
+    return round(best, 1)
+
+
 def time_config(torch, nb, M, N, K, seed, g_std, rotate_bytes=512 << 20, target_s=0.02, trials=5, op="grad_a",
                 splits=1):
     """Median per-call time of nf4_grad_a (or, op="forward", nf4_forward) over rotated input sets (each set:
@@ -539,6 +559,7 @@ def main():
                                                                PEAK_FP16_TFLOPS, 4)}
     log(f"[bench] grouped step {ms_grouped:.2f} ms ({grouped['tflops']:.1f} TFLOP/s)")
 
+    copy_gbs = copy_bandwidth(torch)
     per_config = None if args.no_configs else per_config_table(torch, nb)
     per_config_fwd = None if args.no_configs else per_config_table(torch, nb, op="forward")
     per_config_rms = None if args.no_configs else per_config_rms_norm(torch, nb)
@@ -566,6 +587,7 @@ def main():
             "frac_of_roofline_time": round(step_roof * 1e3 / ms_per_step, 4),
             "device": props.name,
             "cus": props.multi_processor_count,
+            "copy_gbs_measured": copy_gbs,
         },
         "roofline": roof,
         "grouped_step": grouped,

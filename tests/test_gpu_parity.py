@@ -470,6 +470,19 @@ def test_grad_a_operand_rounding_of_grad_out(lib):
     assert np.array_equal(gpu, want)
 
 
+def test_grad_a_joint_permutation_of_n(lib):
+    """Permuting the reduction index n jointly in W (rows of codes and scales) and in grad_out (columns)
+    leaves grad_A unchanged up to rounding order: both results within the oracle's bound."""
+    M, N, K = 300, 1024, 384
+    g, s, b = random_inputs(M, N, K, seed=61)
+    perm = np.random.default_rng(62).permutation(N)
+    ref, S = oracle.grad_a(g, s, b, M, N, K)
+    base = host(lib.grad_a(dev(g), dev(s), dev(b)))
+    permuted = host(lib.grad_a(dev(np.ascontiguousarray(g[:, perm])), dev(s[perm]), dev(b[perm])))
+    assert_within_bound(base, ref, S, "unpermuted")
+    assert_within_bound(permuted, ref, S, "n permuted jointly")
+
+
 def test_grad_a_adjoint_identity(lib):
     M, N, K = 48, 700, 384
     g, s, b = random_inputs(M, N, K, seed=31)
