@@ -39,7 +39,9 @@
  *     device buffer per (device, stream) that has needed one, grown on
  *     demand and held until nf4_release_workspaces().  Calls on one stream
  *     share it (they run in order); concurrent calls on different streams
- *     use different buffers and are safe.  A stream handle that is destroyed
+ *     use different buffers and are safe.  Calls on one stream must be issued
+ *     from one host thread at a time (a call that grows the buffer frees the
+ *     old one in stream order, before work another thread enqueues later).  A stream handle that is destroyed
  *     while its calls are still running must not be reused by a new stream
  *     before they finish (the new stream would inherit the buffer).
  */
