@@ -120,6 +120,37 @@ def test_forward_one_hot_rows_give_fp16_weight_columns(lib):
     assert np.array_equal(gpu, w16[:, picks].T)
 
 
+@pytest.mark.parametrize("kernel", ["tile", "stream"])
+def test_forward_fp16_edge_values(lib, kernel):
+    """Activations at RNE ties, fp16 subnormals, values rounding to zero and +-65504 against a single unit
+    weight give fp16(a) exactly; one-hot activations against weights whose scales run from 1e-7 to 65000
+    (fp16 subnormal to near-maximum weights) give fp16(fl32(scale * level)) exactly; both kernels."""
+    M, N, K = 16, 128, 384
+    edge = np.array([0.0, -0.0, 1e-8, 2.9802322e-08, 3.0e-8, 5.9604645e-08, 1e-6, 6.0975552e-05,
+                     1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 65504.0, -65504.0, 65519.0, 2049.0, 0.1,
+                     -0.3333333], dtype=np.float32)
+    n0, k0 = 45, 201
+    b = np.full((N, K // 2), 0x77, dtype=np.uint8)
+    b[n0, k0 // 2] = 0xF7 if k0 % 2 else 0x7F
+    s = np.ones((N, K // 64), dtype=np.float32)
+    a = synth.grad_out_normal(M, K, seed=66)
+    a[:, k0] = edge
+    gpu = host(lib.forward(dev(a), dev(s), dev(b), splits=1, kernel=kernel))
+    want = np.zeros((M, N), dtype=np.float32)
+    want[:, n0] = edge.astype(np.float16).astype(np.float32)
+    assert np.array_equal(gpu, want)
+    b = synth.random_code_bytes(N, K, seed=67)
+    scale_set = np.array([1e-7, 3e-6, 5e-5, 6.1e-5, 1.0, 3e4, 65000.0], dtype=np.float32)
+    s = scale_set[np.random.default_rng(68).integers(0, len(scale_set), size=(N, K // 64))]
+    a = np.zeros((M, K), dtype=np.float32)
+    picks = np.random.default_rng(69).integers(0, K, size=M)
+    a[np.arange(M), picks] = 1.0
+    gpu = host(lib.forward(dev(a), dev(s), dev(b), splits=2, kernel=kernel))
+    w16 = oracle.dequant(s, b, N, K).astype(np.float16).astype(np.float32)
+    assert np.all(np.isfinite(gpu))
+    assert np.array_equal(gpu, w16[:, picks].T)
+
+
 def test_forward_power_of_two_scaling_is_exact(lib):
     M, N, K = 40, 256, 512
     a, s, b = fwd_inputs(M, N, K, seed=97)

@@ -470,6 +470,61 @@ def test_grad_a_operand_rounding_of_grad_out(lib):
     assert np.array_equal(gpu, want)
 
 
+# fp32 values whose fp16 images probe round-to-nearest-even, the subnormal range and the top of the range
+_FP16_EDGE_VALUES = np.array([
+    0.0, -0.0, 1e-8, 2.9802322e-08, 3.0e-8, 5.9604645e-08, 8.9406967e-08, 1e-6, -3.3e-6, 6.0975552e-05,
+    6.1035156e-05, 1.0, 1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, -(1.0 + 2.0 ** -10), 2.0 ** -14 * 1.5,
+    1024.5, 2049.0, 65504.0, -65504.0, 65519.0, -65519.0, 0.1, -0.3333333], dtype=np.float32)
+
+_PLANS = [(None, 1, 1), ("tile", 1, 1), ("tile", 2, 2), ("wide", 1, 1), ("wide", 2, 1), ("wide16", 1, 2),
+          ("skinny", 0, 2), ("stream", 0, 2)]
+
+
+@pytest.mark.parametrize("kernel,rb,splits", _PLANS, ids=lambda v: str(v))
+def test_grad_a_fp16_edge_values_of_grad_out_every_kernel(lib, kernel, rb, splits):
+    """A single weight 1.0 at (n0, k0) and grad_out column n0 holding RNE ties, fp16 subnormals, values that
+    round to zero and to +-65504: column k0 of grad_A is fp16(grad_out[:, n0]) exactly and every other
+    column is zero, in every kernel (the conversion is RNE and keeps subnormals)."""
+    M = 16 if kernel in ("skinny", "stream") else 48
+    N, K = 128, 256
+    n0, k0 = 77, 130
+    b = np.full((N, K // 2), 0x77, dtype=np.uint8)
+    b[n0, k0 // 2] = 0xF7 if k0 % 2 else 0x7F
+    s = np.ones((N, K // 64), dtype=np.float32)
+    g = synth.grad_out_normal(M, N, seed=55)
+    g[:, n0] = np.resize(_FP16_EDGE_VALUES, M)
+    if kernel is None:
+        gpu = host(lib.grad_a(dev(g), dev(s), dev(b)))
+    else:
+        gpu = host(lib.grad_a_forced(dev(g), dev(s), dev(b), kernel, rb=rb, splits=splits))
+    want = np.zeros((M, K), dtype=np.float32)
+    want[:, k0] = g[:, n0].astype(np.float16).astype(np.float32)
+    assert np.all(np.isfinite(gpu))
+    assert np.array_equal(gpu, want)
+
+
+@pytest.mark.parametrize("kernel,rb,splits", _PLANS, ids=lambda v: str(v))
+def test_grad_a_one_hot_rows_fp16_subnormal_and_large_weights(lib, kernel, rb, splits):
+    """Scales from 1e-7 to 65000 make the dequantised weights span fp16 subnormals (and values that round
+    to zero) up to near the fp16 maximum: one-hot grad_out rows give fp16(fl32(scale * level)) rows
+    exactly in every kernel."""
+    M = 16 if kernel in ("skinny", "stream") else 40
+    N, K = 128, 384
+    b = synth.random_code_bytes(N, K, seed=56)
+    scale_set = np.array([1e-7, 3e-6, 5e-5, 6.1e-5, 1.0, 3e4, 65000.0], dtype=np.float32)
+    s = scale_set[np.random.default_rng(57).integers(0, len(scale_set), size=(N, K // 64))]
+    g = np.zeros((M, N), dtype=np.float32)
+    picks = np.random.default_rng(58).integers(0, N, size=M)
+    g[np.arange(M), picks] = 1.0
+    if kernel is None:
+        gpu = host(lib.grad_a(dev(g), dev(s), dev(b)))
+    else:
+        gpu = host(lib.grad_a_forced(dev(g), dev(s), dev(b), kernel, rb=rb, splits=splits))
+    w16 = oracle.dequant(s, b, N, K).astype(np.float16).astype(np.float32)
+    assert np.all(np.isfinite(gpu))
+    assert np.array_equal(gpu, w16[picks])
+
+
 def test_grad_a_joint_permutation_of_n(lib):
     """Permuting the reduction index n jointly in W (rows of codes and scales) and in grad_out (columns)
     leaves grad_A unchanged up to rounding order: both results within the oracle's bound."""
