@@ -93,11 +93,18 @@ def run_step(nb, weights, gouts, outs, events=None):
                 nb.grad_a(gouts[p], s, c, out=outs[p])
 
 
-def run_step_grouped(nb, weights, gouts, outs):
-    """The same step as 28 grouped calls: each layer's 7 projections in one nf4_grad_a_grouped call."""
+# Projections whose grad_out becomes available together in a layer's backward pass: the MLP output
+# projection first, then its two input projections, then the attention output, then q, k and v.
+DEPENDENCY_GROUPS = [["down"], ["up", "gate"], ["o"], ["v", "k", "q"]]
+
+
+def run_step_grouped(nb, weights, gouts, outs, groups=None):
+    """The same step with grouped calls: by default each layer's 7 projections in one nf4_grad_a_grouped
+    call (28 calls); with `groups`, one call per group of projections per layer."""
     for layer in range(LAYERS - 1, -1, -1):
-        probs = [(gouts[p],) + tuple(weights[(layer, p)]) for p in BACKWARD_ORDER]
-        nb.grad_a_grouped(probs, outs=[outs[p] for p in BACKWARD_ORDER])
+        for grp in (groups or [BACKWARD_ORDER]):
+            probs = [(gouts[p],) + tuple(weights[(layer, p)]) for p in grp]
+            nb.grad_a_grouped(probs, outs=[outs[p] for p in grp])
 
 
 def kernel_name_for(plan, N=None):
@@ -542,19 +549,27 @@ def main():
             "share_of_step_time": round(dsec / (ms_total * 1e-3), 4),
             "kernel_source_digest": source_digest()}
 
-    # the same step with each layer's projections in one grouped call
-    for _ in range(max(1, args.warmup)):
-        run_step_grouped(nb, weights, gouts, outs)
-    torch.cuda.synchronize()
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
-    g0.record()
-    for _ in range(args.steps):
-        run_step_grouped(nb, weights, gouts, outs)
-    g1.record()
-    torch.cuda.synchronize()
-    ms_grouped = g0.elapsed_time(g1) / args.steps
+    # the same step with grouped calls: each layer's projections in one call, and in the groups a
+    # backward pass makes available together
+    def time_grouped(groups):
+        for _ in range(max(1, args.warmup)):
+            run_step_grouped(nb, weights, gouts, outs, groups)
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            run_step_grouped(nb, weights, gouts, outs, groups)
+        g1.record()
+        torch.cuda.synchronize()
+        return g0.elapsed_time(g1) / args.steps
+    ms_grouped = time_grouped(None)
+    ms_dep = time_grouped(DEPENDENCY_GROUPS)
+    log(f"[bench] dependency-grouped step {ms_dep:.2f} ms ({step_flops / (ms_dep * 1e-3) / 1e12:.1f} TFLOP/s)")
     grouped = {"ms_per_step": round(ms_grouped, 3), "tflops": round(step_flops / (ms_grouped * 1e-3) / 1e12, 2),
+               "dependency_grouped": {"groups": DEPENDENCY_GROUPS, "calls_per_step": LAYERS * len(DEPENDENCY_GROUPS),
+                                      "ms_per_step": round(ms_dep, 3),
+                                      "tflops": round(step_flops / (ms_dep * 1e-3) / 1e12, 2)},
                "calls_per_step": LAYERS, "frac_of_peak": round(step_flops / (ms_grouped * 1e-3) / 1e12 /
                                                                PEAK_FP16_TFLOPS, 4)}
     log(f"[bench] grouped step {ms_grouped:.2f} ms ({grouped['tflops']:.1f} TFLOP/s)")
