@@ -5,10 +5,13 @@ kernels of ``libnf4bwd.so``.  PyTorch supplies device memory and the current
 stream.  Importing this module loads the in-tree library and fails loudly if
 it is missing; there is no fallback of any kind.
 
-    grad_a(grad_out, scales, codes)  -> fp32 [M, K]
-    forward(a, scales, codes)        -> fp32 [M, N]   (the same layer's forward product)
-    dequant(scales, codes, N, K)     -> fp32 [N, K]
-    pack(w)                          -> (scales fp32 [N, K/64], codes uint8 [N, K/2])
+    grad_a(grad_out, scales, codes)          -> fp32 [M, K]
+    grad_a_grouped([(grad_out, scales, codes), ...])  -> [fp32 [M, K_i], ...]  (shared M, up to 8)
+    forward(a, scales, codes)                -> fp32 [M, N]   (the same layer's forward product)
+    dequant(scales, codes, N, K)             -> fp32 [N, K]
+    pack(w)                                  -> (scales fp32 [N, K/64], codes uint8 [N, K/2])
+    rms_norm_backward(x, gamma, rms, dy)     -> (dx fp32 [rows, H], dgamma fp32 [H])
+    grad_a_plan(M, N, K), grad_a_forced(...), release_workspaces()
 
 Tensors must be contiguous, on the current CUDA (HIP) device, 16-byte
 aligned, with the dtypes and shapes the C ABI states.
