@@ -21,7 +21,7 @@ the 256 MB Infinity Cache; `per_config_forward` the same layers' forward
 product and `per_config_rms_norm` the RMSNorm backward (algorithmic GB/s).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-configs]
-       python bench.py --forward-configs | --unfused-configs | --rmsnorm-configs   (side tables, one JSON line)
+       python bench.py --forward-configs | --unfused-configs | --rmsnorm-configs | --aux-configs   (side tables)
        python bench.py --one M,N,K [--steps K] [--warmup W]   (one shape, for counter collection)
        python bench.py --copy-calibration   (1 GiB device copy, for counter scaling)
 """
@@ -368,6 +368,41 @@ def per_config_rms_norm(torch, nb, rotate_bytes=512 << 20, target_s=0.02, trials
     return out
 
 
+def per_config_aux(torch, nb, trials=5):
+    """nf4_dequant and nf4_pack on the full step's largest weight (18944 x 3584), HBM-bound: algorithmic
+    bytes (dequant reads codes and scales and writes fp32 weights; pack the reverse) per median call."""
+    N, K = 18944, 3584
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    ws = [torch.empty((N, K), device="cuda").normal_(0.0, 0.02, generator=gen) for _ in range(2)]
+    packed = [nb.pack(w) for w in ws]
+    outs = [torch.empty((N, K), device="cuda") for _ in range(2)]
+    code_bytes = N * K // 2 + N * K // 16
+    res = {}
+    for name, fn, by in [("dequant", lambda i: nb.dequant(*packed[i % 2], out=outs[i % 2]), code_bytes + 4 * N * K),
+                         ("pack", lambda i: nb.pack(ws[i % 2], *packed[i % 2]), 4 * N * K + code_bytes)]:
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        tt = []
+        for _ in range(trials):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(10):
+                fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            tt.append(e0.elapsed_time(e1) * 1e-3 / 10)
+        tt.sort()
+        med = tt[len(tt) // 2]
+        res[name] = {"N": N, "K": K, "us": round(med * 1e6, 2), "alg_bytes": by, "gbs": round(by / med / 1e9, 1),
+                     "frac_of_hbm": round(by / med / 1e9 / PEAK_HBM_GBS, 4)}
+        log(f"[bench] {name} {N}x{K}: {med * 1e6:.1f} us  {by / med / 1e9:.0f} GB/s")
+    del ws, packed, outs
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline_rms_norm(target_s=5.0):
     """The fp64 RMSNorm-backward oracle on the 8192 x 3584 shape, repeated until about `target_s` seconds."""
     import numpy as np
@@ -440,6 +475,8 @@ def main():
                     help="only the fused-against-unfused comparison table (one JSON line)")
     ap.add_argument("--forward-configs", action="store_true",
                     help="only the forward product's per-config table and its CPU oracle baseline (one JSON line)")
+    ap.add_argument("--aux-configs", action="store_true",
+                    help="only nf4_dequant and nf4_pack throughput on the full step's largest weight (one JSON line)")
     ap.add_argument("--rmsnorm-configs", action="store_true",
                     help="only the RMSNorm backward's per-shape table and its CPU oracle baseline (one JSON line)")
     ap.add_argument("--one", type=str, default=None, metavar="M,N,K",
@@ -483,6 +520,9 @@ def main():
         return
     if args.unfused_configs:
         print(json.dumps({"per_config_unfused": per_config_unfused(torch, nb)}), flush=True)
+        return
+    if args.aux_configs:
+        print(json.dumps({"per_config_aux": per_config_aux(torch, nb)}), flush=True)
         return
     if args.rmsnorm_configs:
         rec = {"per_config_rms_norm": per_config_rms_norm(torch, nb),
