@@ -618,6 +618,7 @@ def main():
     per_config = None if args.no_configs else per_config_table(torch, nb)
     per_config_fwd = None if args.no_configs else per_config_table(torch, nb, op="forward")
     per_config_rms = None if args.no_configs else per_config_rms_norm(torch, nb)
+    per_config_aux_ = None if args.no_configs else per_config_aux(torch, nb)
     cpu = None if args.no_cpu else cpu_baseline()
 
     rec = {
@@ -650,6 +651,7 @@ def main():
         "per_config": per_config,
         "per_config_forward": per_config_fwd,
         "per_config_rms_norm": per_config_rms,
+        "per_config_aux": per_config_aux_,
     }
     print(json.dumps(rec), flush=True)
 
