@@ -7,7 +7,8 @@
 //
 // * A workgroup (8 waves) owns a 128-column strip of grad_A over an N-chunk;
 //   the waves take interleaved k-steps of 32 rows of N and are summed in a
-//   fixed order at the end (LDS), the N-chunks by the split reduction.
+//   fixed order at the end (LDS); the N-chunks' partials are summed, in chunk
+//   order, by the last workgroup of the strip to finish.
 // * Per k-step a wave builds the fp16 weight tables of its 32 rows x 2 scale
 //   blocks in its own LDS area -- the 16 values fp16(fl32(scale * level)) a
 //   code can stand for -- then decodes every weight with one 16-bit table
@@ -46,9 +47,11 @@ template <bool VEC_A>
 __global__ __launch_bounds__(512, 2) void grad_a_stream_kernel(const float* __restrict__ G,
                                                                const float* __restrict__ S,
                                                                const uint32_t* __restrict__ C32,
-                                                               float* __restrict__ out, int M, int N, int K,
-                                                               int n_chunk, int tiles_k) {
+                                                               float* out, float* __restrict__ grad_a,
+                                                               uint32_t* __restrict__ counters, int M, int N, int K,
+                                                               int n_chunk, int tiles_k, int splits) {
   __shared__ __attribute__((aligned(16))) uint32_t smem[kSkRedBytes / 4];
+  __shared__ uint32_t last_in_strip;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -217,9 +220,47 @@ __global__ __launch_bounds__(512, 2) void grad_a_stream_kernel(const float* __re
       s += __builtin_bit_cast(floatx4,
                               lds_load_u32x4(smem, (uint32_t)((w * 16 + row) * kSkinnyBK + 4 * c4) * 4u));
     const int col = k0 + 4 * c4;
-    if (row < M && col < K) {
-      float* dst = out + (size_t)split * (size_t)M * (size_t)K;
-      *reinterpret_cast<floatx4*>(dst + (size_t)row * (size_t)K + col) = s;
+    const bool mine = row < M && col < K;
+    const uint32_t at = 4u * ((uint32_t)row * (uint32_t)K + (uint32_t)col);  // byte offset in one partial
+    const uint32_t part = 4u * (uint32_t)M * (uint32_t)K;                    // bytes per partial
+    if (splits == 1 || counters == nullptr) {
+      if (mine) *reinterpret_cast<floatx4*>(reinterpret_cast<char*>(out) + (size_t)split * part + at) = s;
+    } else {
+      // Split reduction by the strip's last workgroup to finish.  The partials
+      // are stored and loaded with device-scope coherence (sc1: they bypass
+      // the XCDs' separate L2s), each wave waits for its stores to complete
+      // before the workgroup's arrival is counted, and the workgroup that
+      // sees the count reach `splits` sums the partials in split order,
+      // ((p0 + p1) + p2) + ..., so the result does not depend on which
+      // workgroup that is; it then resets the counter for the next call.
+      // (A device-scope fence instead writes back and invalidates the whole
+      // L2 per wave: measured 6x slower for the whole kernel.)
+      constexpr int kDevice = 16;  // buffer cache policy: sc1
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(out, (uint32_t)splits * part);
+      if (mine) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s), rp, at, (uint32_t)split * part,
+                                                       kDevice);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));  // vmcnt(0): the stores are complete
+      __syncthreads();
+      if (tid == 0) last_in_strip = atomicAdd(&counters[kt], 1u) == (uint32_t)(splits - 1);
+      __syncthreads();
+      if (!last_in_strip) return;
+      if (mine) {
+        floatx4 t = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rp, at, 0, kDevice));
+        for (int sp = 1; sp < splits; sp += 8) {
+          floatx4 v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (sp + u < splits)
+              v[u] = __builtin_bit_cast(floatx4,
+                                        __builtin_amdgcn_raw_buffer_load_b128(rp, at, (uint32_t)(sp + u) * part, kDevice));
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (sp + u < splits) t += v[u];
+        }
+        *reinterpret_cast<floatx4*>(reinterpret_cast<char*>(grad_a) + at) = t;
+      }
+      if (tid == 0) __hip_atomic_store(&counters[kt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -230,13 +271,15 @@ bool stream_kernel_supported(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_grad_a_stream(int grid, const float* grad_out, const float* scales, const uint32_t* codes,
-                                float* dst, int M, int N, int K, int n_chunk, int tiles_k, hipStream_t stream) {
+                                float* dst, float* grad_a, uint32_t* counters, int M, int N, int K, int n_chunk,
+                                int tiles_k, int splits, hipStream_t stream) {
+  if (counters != nullptr && tiles_k > kWsCounters) return hipErrorInvalidValue;
   if ((N & 3) == 0)
-    hipLaunchKernelGGL(grad_a_stream_kernel<true>, dim3(grid), dim3(512), 0, stream, grad_out, scales, codes, dst, M,
-                       N, K, n_chunk, tiles_k);
+    hipLaunchKernelGGL(grad_a_stream_kernel<true>, dim3(grid), dim3(512), 0, stream, grad_out, scales, codes, dst,
+                       grad_a, counters, M, N, K, n_chunk, tiles_k, splits);
   else
     hipLaunchKernelGGL(grad_a_stream_kernel<false>, dim3(grid), dim3(512), 0, stream, grad_out, scales, codes, dst,
-                       M, N, K, n_chunk, tiles_k);
+                       grad_a, counters, M, N, K, n_chunk, tiles_k, splits);
   return hipGetLastError();
 }
 

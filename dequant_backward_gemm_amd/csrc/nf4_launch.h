@@ -39,8 +39,12 @@ bool make_plan(int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, 
 
 // Split-N workspace of at least `bytes` for calls on `stream` (cached per
 // device and stream, grown with a stream-ordered allocation); and the release
-// of every cached workspace (drains the devices that hold one).
-hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** out);
+// of every cached workspace (drains the devices that hold one).  `counters`
+// (optional) receives the buffer's kWsCounters 32-bit arrival counters: zero
+// between calls on the stream, and a kernel that counts on them must leave
+// them at zero.
+constexpr int kWsCounters = 4096;
+hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** out, uint32_t** counters = nullptr);
 hipError_t release_workspaces();
 
 // Launch a given plan.
@@ -136,8 +140,13 @@ hipError_t launch_nf4_forward(const float* a, const float* scales, const uint8_t
 // 32-bit byte offsets.
 constexpr int kStreamBK = 128;
 bool stream_kernel_supported(int64_t M, int64_t N, int64_t K);
+// With splits > 1, dst holds the splits' partials and, when `counters` (one
+// per strip, zero on entry and on exit) is given, the last workgroup of each
+// strip to finish sums them in split order into grad_a; without counters the
+// caller runs the split reduction.
 hipError_t launch_grad_a_stream(int grid, const float* grad_out, const float* scales, const uint32_t* codes,
-                                float* dst, int M, int N, int K, int n_chunk, int tiles_k, hipStream_t stream);
+                                float* dst, float* grad_a, uint32_t* counters, int M, int N, int K, int n_chunk,
+                                int tiles_k, int splits, hipStream_t stream);
 
 // Kernel launchers of nf4_grad_a.hip (tile, skinny, split reduction, zero fill).
 hipError_t launch_grad_a_tile(int rb, bool fast, int grid, const float* grad_out, const float* scales,

@@ -13,7 +13,9 @@ namespace nf4 {
 // stream-ordered allocation and kept for later calls on that stream.  Calls
 // on one stream run in order, so they can share it; calls on different
 // streams get different buffers.  (A stream-ordered allocate/free pair per
-// call cost more host time than a skinny call's kernels take.)
+// call cost more host time than a skinny call's kernels take.)  Each buffer
+// starts with kWsCounters arrival counters, zeroed once when the buffer is
+// allocated; a kernel that uses them leaves them at zero again.
 namespace {
 struct Workspace {
   int device;
@@ -25,17 +27,22 @@ std::mutex g_ws_mutex;
 std::vector<Workspace> g_ws;
 }  // namespace
 
-hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** out) {
+hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** out, uint32_t** counters) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  const size_t want = (bytes + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);  // whole MiB
+  constexpr size_t kHeader = (size_t)kWsCounters * sizeof(uint32_t);
+  const size_t want = (kHeader + bytes + (1u << 20) - 1) & ~(size_t)((1u << 20) - 1);  // whole MiB
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   Workspace* w = nullptr;
   for (auto& x : g_ws)
     if (x.device == dev && x.stream == stream) w = &x;
-  if (w != nullptr && w->bytes >= bytes) {
-    *out = w->ptr;
+  auto hand_out = [&]() {
+    *out = static_cast<char*>(w->ptr) + kHeader;
+    if (counters != nullptr) *counters = static_cast<uint32_t*>(w->ptr);
+  };
+  if (w != nullptr && w->bytes >= kHeader + bytes) {
+    hand_out();
     return hipSuccess;
   }
   if (w == nullptr) {
@@ -55,7 +62,10 @@ hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** out) {
     return e;
   }
   w->bytes = want;
-  *out = w->ptr;
+  // the counters start at zero (a fill kernel, in stream order)
+  e = launch_fill_zero(1, static_cast<float*>(w->ptr), (int64_t)(kHeader / 16), stream);
+  if (e != hipSuccess) return e;
+  hand_out();
   return hipSuccess;
 }
 
@@ -92,28 +102,30 @@ GradAPlan plan_grad_a(int64_t M, int64_t N, int64_t K) {
   }
   const int64_t tiles_k = cdiv(K, 256);
   if (M <= 16 && stream_kernel_supported(M, N, K)) {
-    // Streaming kernel: 128-column strips x N-chunks, two workgroups per CU.
-    // Pick the chunk count by a bandwidth model: the weight stream runs at
-    // the chip rate spread over the workgroup slots in use, in whole rounds
-    // of two workgroups per CU (a round started by a few leftover
-    // workgroups costs as much as a full one: measured 532 workgroups 30%
-    // slower than 504); a split adds its partials (written and read once)
-    // and the reduce launch.  Chunks shorter than one k-step per wave leave
-    // waves idle and are not considered.
+    // Streaming kernel: 128-column strips x N-chunks, up to two workgroups
+    // per CU at a time.  The loop is bound by each CU's LDS table reads, and
+    // its time follows the busiest SIMD: wave w of a workgroup takes k-steps
+    // w, w + 8, ... of its chunk, waves w and w + 4 share a SIMD, and the
+    // workgroups a CU is given add up.  Fitted to split sweeps on MI355X
+    // (M = 1..16; N x K = 18944 x 3584, 3584 x 18944, 14336 x 4096,
+    // 4096 x 14336, 4096 x 11008, 8960 x 1536, 1536 x 1536): ~0.55 us per
+    // k-step of that SIMD load, ~1.5 us per workgroup per CU beyond the
+    // first, ~0.2 us per further chunk (partials and their sum by the
+    // strip's last workgroup).  E.g. 18944 x 3584: 9 chunks (252
+    // workgroups, 17 steps per SIMD) 16.5 us, 18 chunks (504, 2 x 9) 18.2.
     const int64_t tk = cdiv(K, kStreamBK);
-    const double bw = 5.0e12;
-    const double stream_bytes = (double)N * (double)K * (0.5 + 1.0 / 16.0) + 4.0 * (double)M * (double)(N + K);
-    const int64_t slots = 2 * kCUs;
+    auto wave_steps = [](int64_t steps, int w) { return steps > w ? (steps - w + 7) / 8 : 0; };
     double best = 1e30;
     for (int64_t s = 1; s <= 64; ++s) {
       const int64_t chunk = cdiv(cdiv(N, s), 32) * 32;
       const int64_t se = cdiv(N, chunk);
-      if (se != s || (se > 1 && chunk < 256)) continue;
+      if (se != s) continue;
+      const int64_t steps = chunk / 32;  // k-steps of the largest chunk
+      int64_t simd = 0;
+      for (int j = 0; j < 4; ++j) simd = std::max(simd, wave_steps(steps, j) + wave_steps(steps, j + 4));
       const int64_t grid = tk * se;
-      const double rounds = (double)cdiv(grid, slots);
-      // (each further round also pays a ramp of about 1.5 us)
-      double t = stream_bytes / bw * (rounds * slots) / (double)grid + 3e-6 + (rounds - 1.0) * 1.5e-6;
-      if (se > 1) t += 2.0 * (double)se * (double)M * (double)K * 4.0 / bw + 4e-6;
+      const int64_t per_cu = cdiv(grid, kCUs);
+      const double t = 0.55e-6 * (double)(per_cu * simd) + 1.5e-6 * (double)(per_cu - 1) + 0.2e-6 * (double)(se - 1);
       if (t < best * 0.999) {
         best = t;
         p.kernel = 4;
@@ -271,6 +283,11 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
   float* ws = nullptr;
   void* frags = nullptr;
   void* bfrags = nullptr;
+  uint32_t* counters = nullptr;
+  // the streaming kernel sums its own split partials (per-strip arrival counters;
+  // 32-bit byte offsets into the partials)
+  const bool fused_reduce = p.kernel == 4 && p.splits > 1 && cdiv(K, kStreamBK) <= kWsCounters &&
+                            (uint64_t)p.splits * (uint64_t)M * (uint64_t)K * 4 < (1ull << 32);
   {
     // workspace: split partials, then (fragment-fed wide kernel) the fp16 A fragments
     const size_t part = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)K * sizeof(float) : 0;
@@ -280,7 +297,8 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
     const size_t bfrag = p.kernel == 6 ? unfused_bfrag_bytes(N, K) : p.kernel == 7 ? streamk_slot_bytes(p.grid) : 0;
     if (part + frag + bfrag > 0) {
       char* base = nullptr;
-      hipError_t e = stream_workspace(stream, part_al + frag_al + bfrag, reinterpret_cast<void**>(&base));
+      hipError_t e = stream_workspace(stream, part_al + frag_al + bfrag, reinterpret_cast<void**>(&base),
+                                      fused_reduce ? &counters : nullptr);
       if (e != hipSuccess) return e;
       if (part) ws = reinterpret_cast<float*>(base);
       if (frag) frags = base + part_al;
@@ -293,8 +311,8 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
   if (p.kernel == 1) {
     e = launch_grad_a_skinny(p.grid, grad_out, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk, tiles_k, stream);
   } else if (p.kernel == 4) {
-    e = launch_grad_a_stream(p.grid, grad_out, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
-                             (int)cdiv(K, kStreamBK), stream);
+    e = launch_grad_a_stream(p.grid, grad_out, scales, c32, dst, grad_a, counters, (int)M, (int)N, (int)K, p.n_chunk,
+                             (int)cdiv(K, kStreamBK), p.splits, stream);
   } else if (p.kernel == 6) {
     e = launch_grad_a_unfused(p.grid, grad_out, frags, bfrags, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
                               (int)cdiv(M, wide_tile_rows(1)), (int)cdiv(K, wide_tile_cols(1)), stream);
@@ -315,7 +333,7 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
                            (int)cdiv(M, 128 * p.rb), tiles_k, stream);
   }
   if (e != hipSuccess) return e;
-  if (p.splits > 1) {
+  if (p.splits > 1 && !fused_reduce) {
     const int64_t n4 = M * K / 4;
     const int grid = (int)std::min<int64_t>(cdiv(n4, 256), 8192);
     e = launch_grad_a_reduce(grid, ws, grad_a, n4, p.splits, stream);

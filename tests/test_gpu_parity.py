@@ -305,6 +305,51 @@ def test_grad_a_stream_deterministic(lib):
         assert np.array_equal(r1.view(np.uint32), r2.view(np.uint32))
 
 
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+@pytest.mark.parametrize("M,N,K,splits", [(16, 3000, 512, 4), (3, 4100, 384, 7), (8, 2048, 640, 64),
+                                          (1, 3584, 18944, 3), (16, 18944, 3584, 18)])
+def test_grad_a_stream_split_sum_is_chunk_partials_in_order(lib, M, N, K, splits):
+    """The streaming kernel's split reduction, done by each strip's last workgroup to finish, equals bit for
+    bit the unsplit kernel run on each N-chunk alone (the same k-steps per wave, hence the same partial),
+    summed on the host in fp32 in chunk order."""
+    g, s, b = random_inputs(M, N, K, seed=7 * M + N + K + splits)
+    chunk = _cdiv(_cdiv(N, splits), 32) * 32
+    full = host(lib.grad_a_forced(dev(g), dev(s), dev(b), "stream", rb=0, splits=splits))
+    acc = None
+    for n0 in range(0, N, chunk):
+        n1 = min(N, n0 + chunk)
+        part = host(lib.grad_a_forced(dev(g[:, n0:n1]), dev(s[n0:n1]), dev(b[n0:n1]), "stream", rb=0, splits=1))
+        acc = part.copy() if acc is None else (acc + part).astype(np.float32)
+    assert _cdiv(N, chunk) > 1
+    assert np.array_equal(full.view(np.uint32), acc.view(np.uint32))
+
+
+def test_grad_a_stream_split_counters_across_calls(lib):
+    """Split calls of different strip and split counts back to back on one stream (they share the
+    workspace's arrival counters): every output written in full (outputs start as NaN), each within the
+    bound, and the second pass bitwise equal to the first."""
+    shapes = [(16, 3000, 512, 4), (8, 5000, 1024, 6), (1, 700, 128, 3), (16, 3000, 512, 11), (4, 9000, 256, 64)]
+    data = [random_inputs(M, N, K, seed=300 + i) for i, (M, N, K, _) in enumerate(shapes)]
+    devs = [(dev(g), dev(s), dev(b)) for g, s, b in data]
+    firsts = []
+    for rnd in range(2):
+        outs = []
+        for (M, N, K, sp), d in zip(shapes, devs):
+            o = torch.full((M, K), float("nan"), device="cuda")
+            outs.append(lib.grad_a_forced(*d, "stream", rb=0, splits=sp, out=o))
+        res = [host(o) for o in outs]
+        for i, ((M, N, K, sp), (g, s, b)) in enumerate(zip(shapes, data)):
+            if rnd == 0:
+                ref, S = oracle.grad_a(g, s, b, M, N, K)
+                assert_within_bound(res[i], ref, S, f"shape {i}")
+                firsts.append(res[i])
+            else:
+                assert np.array_equal(res[i].view(np.uint32), firsts[i].view(np.uint32)), f"shape {i}"
+
+
 PAGE_SHAPES = [(128, 1536, 1536), (64, 256, 128), (16, 64, 64), (512, 1536, 1536), (512, 256, 1536),
                (512, 4608, 1536), (512, 1536, 4608)]
 
