@@ -11,9 +11,17 @@
 //   tiles) over a chunk of K and walks it in steps of 128 k (two scale
 //   blocks).  Per step a lane loads 16 contiguous code bytes of its row per
 //   tile, so one load instruction covers 64 bytes of each of 16 rows and
-//   consecutive steps read consecutive bytes.  A workgroup is 8 such waves;
-//   waves never exchange data, so there is no cross-wave sum and no barrier.
-//   K chunks (splits) go through fp32 partials and the fixed-order reduce.
+//   consecutive steps read consecutive bytes.  A workgroup is 8 such waves
+//   over the same K chunk; each output is one wave's, so there is no
+//   cross-wave sum.  K chunks (splits) go through fp32 partials and the
+//   fixed-order reduce.
+// * The activations of a step (16 rows x 128 k) are the same for all 8
+//   waves, so they are loaded once per workgroup -- one 16-byte load per
+//   thread -- rounded to fp16 and written to LDS in the MFMA A layout (a
+//   double buffer, one barrier per step); each wave then reads its four A
+//   operands from there.  Loaded by every wave instead, at M = 16 they were
+//   8 KiB per wave and step, four times the code bytes, and the kernel took
+//   37 us against 25 at M = 1 on 18944 x 3584.
 // * Decode: a lane's eight weights of one MFMA share a row and a scale block,
 //   so the lane holds that one scale in a register and decodes each weight as
 //   fp16(fl32(scale * level[code])), the level read from a 16-entry fp32
@@ -42,6 +50,7 @@ constexpr int kFsWaves = 8;
 constexpr int kFsTiles = 2;                       // MFMA tiles (16 columns each) per wave
 constexpr int kFsCols = 16 * kFsTiles * kFsWaves;  // columns n of C per workgroup
 constexpr int kFsTabBytes = 64;                   // per wave: the 16 fp32 levels
+constexpr int kFsABytes = 4 * 64 * 16;             // one step's A operands: [u][lane] x 16 B
 
 template <int T>
 __global__ __launch_bounds__(512, 2) void nf4_forward_stream_kernel(const float* __restrict__ A,
@@ -49,7 +58,7 @@ __global__ __launch_bounds__(512, 2) void nf4_forward_stream_kernel(const float*
                                                                     const uint32_t* __restrict__ C32,
                                                                     float* __restrict__ out, int M, int N, int K,
                                                                     int k_chunk, int strips) {
-  __shared__ __attribute__((aligned(16))) uint32_t smem[kFsWaves * kFsTabBytes / 4];
+  __shared__ __attribute__((aligned(16))) uint32_t smem[(kFsWaves * kFsTabBytes + 2 * kFsABytes) / 4];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -79,9 +88,15 @@ __global__ __launch_bounds__(512, 2) void nf4_forward_stream_kernel(const float*
   const uint32_t cvoff = (uint32_t)ci * crow + 16u * (uint32_t)q;
   // scale of lane (ci, q): row ci, block 2s + q / 2
   const uint32_t svoff = (uint32_t)ci * srow + 4u * (uint32_t)(q >> 1);
-  // activations of lane (i = ci, q): row ci, k = 128s + 32q .. + 31
-  const bool arow_ok = ci < M;
-  const uint32_t avoff = ((uint32_t)ci * (uint32_t)K + 32u * (uint32_t)q) * 4u;
+  // activations loaded by thread t: row t / 32, k = 128s + 4 (t % 32) .. + 3;
+  // stored as A operand u of lane (row, k / 32) at half 4 ((t % 32) & 1)
+  const int arow = tid >> 5, af4 = tid & 31;
+  const bool arow_ok = arow < M;
+  const uint32_t avoff = ((uint32_t)arow * (uint32_t)K + 4u * (uint32_t)af4) * 4u;
+  const uint32_t abase = kFsWaves * kFsTabBytes;
+  const uint32_t astore =
+      abase + (uint32_t)((((af4 >> 1) & 3) * 64 + 16 * (af4 >> 3) + arow) * 16 + 8 * (af4 & 1));
+  const uint32_t aread = abase + 16u * (uint32_t)lane;
 
   floatx4 acc[T];
 #pragma unroll
@@ -90,7 +105,7 @@ __global__ __launch_bounds__(512, 2) void nf4_forward_stream_kernel(const float*
   struct Step {
     u32x4 x[T];
     float sc[T];
-    floatx4 a[8];
+    floatx4 a;
   };
   // (steps past the chunk are clamped to its last one: the loads stay
   // unconditional, so the wait counts never depend on a branch)
@@ -105,13 +120,20 @@ __global__ __launch_bounds__(512, 2) void nf4_forward_stream_kernel(const float*
       const uint32_t soff = s_ok ? svoff + (uint32_t)(16 * t) * srow : 0x80000000u;
       d.sc[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, soff, (uint32_t)k0 / 16u, 0));
     }
-    const uint32_t ao = (arow_ok && (q < 2 || hi_ok)) ? avoff : 0x80000000u;
-#pragma unroll
-    for (int v = 0; v < 8; ++v)
-      d.a[v] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(ra, ao + 16u * v, 4u * k0, 0));
+    const uint32_t ao = (arow_ok && (af4 < 16 || hi_ok)) ? avoff : 0x80000000u;
+    d.a = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(ra, ao, 4u * k0, 0));
   };
 
-  auto run_step = [&](const Step& d) {
+  // buffer b of the A double buffer: steps of parity b (a buffer is rewritten
+  // two steps after it was read, with the previous step's barrier between)
+  auto run_step = [&](const Step& d, uint32_t b) {
+    {
+      u32x2 h;
+      h[0] = pack_half2_rne(d.a[0], d.a[1]);
+      h[1] = pack_half2_rne(d.a[2], d.a[3]);
+      lds_store_u32x2(smem, astore + b * kFsABytes, h);
+    }
+    __syncthreads();
     // decode and MFMA; the level reads of MFMA u + 1 are issued before MFMA u's
     // weights are formed
     // (u, t) pairs in the order u * T + t
@@ -136,14 +158,7 @@ __global__ __launch_bounds__(512, 2) void nf4_forward_stream_kernel(const float*
       constexpr int i = decltype(ic)::value;
       constexpr int u = i / T, t = i % T;
       if constexpr (i + 1 < 4 * T) lookup(std::integral_constant<int, i + 1>{}, lk[(i + 1) & 1]);
-      if constexpr (t == 0) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const floatx4 a4 = d.a[2 * u + (p >> 1)];
-          const float lo = a4[2 * (p & 1)], hi = a4[2 * (p & 1) + 1];
-          af[p] = pack_half2_rne(lo, hi);
-        }
-      }
+      if constexpr (t == 0) af = lds_load_u32x4(smem, aread + b * kFsABytes + 1024u * u);
       u32x4 bf;
 #pragma unroll
       for (int p = 0; p < 4; ++p) bf[p] = pack_half2_rne(d.sc[t] * lk[i & 1][2 * p], d.sc[t] * lk[i & 1][2 * p + 1]);
@@ -161,14 +176,14 @@ __global__ __launch_bounds__(512, 2) void nf4_forward_stream_kernel(const float*
     for (; i + 2 <= nsteps; i += 2) {
       load_step(i + 1, s1);
       __builtin_amdgcn_sched_barrier(0);
-      run_step(s0);
+      run_step(s0, 0);
       __builtin_amdgcn_sched_barrier(0);
       load_step(i + 2, s0);
       __builtin_amdgcn_sched_barrier(0);
-      run_step(s1);
+      run_step(s1, 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (i < nsteps) run_step(s0);
+    if (i < nsteps) run_step(s0, 0);
   }
 
   // accumulator lane (ci, q), register r of tile t: row 4q + r, column n0 + 16t + ci
