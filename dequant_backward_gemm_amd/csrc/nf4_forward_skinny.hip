@@ -13,8 +13,9 @@
 //   tile, so one load instruction covers 64 bytes of each of 16 rows and
 //   consecutive steps read consecutive bytes.  A workgroup is 8 such waves
 //   over the same K chunk; each output is one wave's, so there is no
-//   cross-wave sum.  K chunks (splits) go through fp32 partials and the
-//   fixed-order reduce.
+//   cross-wave sum.  K chunks (splits) go through fp32 partials, summed in
+//   chunk order by the last workgroup of the strip to finish (or, without
+//   arrival counters, by the reduce kernel).
 // * The activations of a step (16 rows x 128 k) are the same for all 8
 //   waves, so they are loaded once per workgroup -- one 16-byte load per
 //   thread -- rounded to fp16 and written to LDS in the MFMA A layout (a
@@ -56,9 +57,11 @@ template <int T>
 __global__ __launch_bounds__(512, 2) void nf4_forward_stream_kernel(const float* __restrict__ A,
                                                                     const float* __restrict__ S,
                                                                     const uint32_t* __restrict__ C32,
-                                                                    float* __restrict__ out, int M, int N, int K,
-                                                                    int k_chunk, int strips) {
+                                                                    float* out, float* __restrict__ c,
+                                                                    uint32_t* __restrict__ counters, int M, int N,
+                                                                    int K, int k_chunk, int strips, int splits) {
   __shared__ __attribute__((aligned(16))) uint32_t smem[(kFsWaves * kFsTabBytes + 2 * kFsABytes) / 4];
+  __shared__ uint32_t last_in_strip;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -187,19 +190,72 @@ __global__ __launch_bounds__(512, 2) void nf4_forward_stream_kernel(const float*
   }
 
   // accumulator lane (ci, q), register r of tile t: row 4q + r, column n0 + 16t + ci
+  if (splits == 1 || counters == nullptr) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int col = n0 + 16 * t + ci;
+      if (col < N) {
+        float* dst = out + (size_t)split * (size_t)M * (size_t)N + col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 4 * q + r;
+          const float v = acc[t][r];
+          if (row < M) dst[(size_t)row * (size_t)N] = v;
+        }
+      }
+    }
+    return;
+  }
+  // Split sum by the strip's last workgroup to finish, as in the backward
+  // streaming kernel: partials stored and loaded with device-scope coherence
+  // (sc1, past the XCDs' separate L2s), each wave's stores complete before the
+  // workgroup's arrival is counted, the chunks summed in order
+  // ((p0 + p1) + p2) + ..., the counter reset for the next call.
+  constexpr int kDevice = 16;  // buffer cache policy: sc1
+  const uint32_t part = 4u * (uint32_t)M * (uint32_t)N;  // bytes per partial
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(out, (uint32_t)splits * part);
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int col = n0 + 16 * t + ci;
-    if (col < N) {
-      float* dst = out + (size_t)split * (size_t)M * (size_t)N + col;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * q + r;
-        const float v = acc[t][r];
-        if (row < M) dst[(size_t)row * (size_t)N] = v;
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * q + r;
+      // (the element goes through a scalar first: __builtin_bit_cast of a
+      // vector element reads element 0 whatever the index)
+      const float v = acc[t][r];
+      if (col < N && row < M)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rp,
+                                              4u * ((uint32_t)row * (uint32_t)N + (uint32_t)col),
+                                              (uint32_t)split * part, kDevice);
     }
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));  // vmcnt(0): the stores are complete
+  __syncthreads();
+  if (tid == 0) last_in_strip = atomicAdd(&counters[strip], 1u) == (uint32_t)(splits - 1);
+  __syncthreads();
+  if (!last_in_strip) return;
+  // the strip's M x 256 outputs as float4 (N % 8 == 0: a strip's columns are whole float4s)
+  const int c0 = strip * kFsCols;
+  for (int e = tid; e < M * (kFsCols / 4); e += 64 * kFsWaves) {
+    const int row = e / (kFsCols / 4), col = c0 + 4 * (e % (kFsCols / 4));
+    if (col >= N) continue;
+    const uint32_t at = 4u * ((uint32_t)row * (uint32_t)N + (uint32_t)col);
+    floatx4 sum = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rp, at, 0, kDevice));
+    for (int sp = 1; sp < splits; sp += 8) {
+      floatx4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (sp + u < splits)
+          v[u] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rp, at, (uint32_t)(sp + u) * part,
+                                                                                   kDevice));
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (sp + u < splits) sum += v[u];
+    }
+    *reinterpret_cast<floatx4*>(reinterpret_cast<char*>(c) + at) = sum;
+  }
+  if (tid == 0) __hip_atomic_store(&counters[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 bool forward_stream_supported(int64_t M, int64_t N, int64_t K) {
@@ -210,9 +266,11 @@ bool forward_stream_supported(int64_t M, int64_t N, int64_t K) {
 int forward_stream_strips(int64_t N) { return (int)((N + kFsCols - 1) / kFsCols); }
 
 hipError_t launch_forward_stream(int grid, const float* a, const float* scales, const uint32_t* codes, float* dst,
-                                 int M, int N, int K, int k_chunk, int strips, hipStream_t stream) {
-  hipLaunchKernelGGL(nf4_forward_stream_kernel<kFsTiles>, dim3(grid), dim3(512), 0, stream, a, scales, codes, dst, M,
-                     N, K, k_chunk, strips);
+                                 float* c, uint32_t* counters, int M, int N, int K, int k_chunk, int strips,
+                                 int splits, hipStream_t stream) {
+  if (counters != nullptr && strips > kWsCounters) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(nf4_forward_stream_kernel<kFsTiles>, dim3(grid), dim3(512), 0, stream, a, scales, codes, dst, c,
+                     counters, M, N, K, k_chunk, strips, splits);
   return hipGetLastError();
 }
 

@@ -127,8 +127,13 @@ hipError_t launch_forward(int grid, const float* a, void* frags, const float* sc
 // strips (16 per wave) x K chunks of whole 128-wide steps.
 bool forward_stream_supported(int64_t M, int64_t N, int64_t K);
 int forward_stream_strips(int64_t N);
+// With splits > 1, dst holds the chunks' partials and, when `counters` (one
+// per strip, zero on entry and on exit) is given, the last workgroup of each
+// strip to finish sums them in chunk order into c; without counters the
+// caller runs the reduction.
 hipError_t launch_forward_stream(int grid, const float* a, const float* scales, const uint32_t* codes, float* dst,
-                                 int M, int N, int K, int k_chunk, int strips, hipStream_t stream);
+                                 float* c, uint32_t* counters, int M, int N, int K, int k_chunk, int strips,
+                                 int splits, hipStream_t stream);
 // kernel: -1 picks (streaming for M <= 16 where supported, else tiles), 0 tiles, 1 streaming;
 // splits <= 0 picks the K chunk count.
 constexpr int kForwardAuto = -1, kForwardTile = 0, kForwardStream = 1;

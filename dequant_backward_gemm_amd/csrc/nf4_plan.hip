@@ -357,18 +357,19 @@ static hipError_t launch_nf4_forward_stream(const float* a, const float* scales,
     chunk = cdiv(cdiv(K, splits), 128) * 128;
     se = cdiv(K, chunk);
   } else {
-    const double bw = 5.0e12;
-    const double stream_bytes = (double)N * (double)K * (0.5 + 1.0 / 16.0) + 4.0 * (double)M * (double)(N + K);
-    const int64_t slots = 2 * kCUs;
+    // Same per-SIMD load model as the backward streaming kernel: all 8 waves
+    // of a workgroup walk its whole chunk (two waves per SIMD), ~0.55 us per
+    // 128-k step of that load times the workgroups per CU, ~1.5 us per
+    // workgroup per CU beyond the first, ~0.2 us per further chunk, plus the
+    // partials (M x N fp32 per chunk) written and read once at ~5 TB/s.
     double best = 1e30;
     for (int64_t s = 1; s <= 64; ++s) {
       const int64_t ch = cdiv(cdiv(K, s), 128) * 128;
       const int64_t e = cdiv(K, ch);
-      if (e != s || (e > 1 && ch < 256)) continue;
-      const int64_t grid = strips * e;
-      const double rounds = (double)cdiv(grid, slots);
-      double t = stream_bytes / bw * (rounds * slots) / (double)grid + 3e-6 + (rounds - 1.0) * 1.5e-6;
-      if (e > 1) t += 2.0 * (double)e * (double)M * (double)N * 4.0 / bw + 4e-6;
+      if (e != s) continue;
+      const int64_t per_cu = cdiv(strips * e, kCUs);
+      double t = 0.55e-6 * (double)(per_cu * 2 * (ch / 128)) + 1.5e-6 * (double)(per_cu - 1) + 0.2e-6 * (double)(e - 1);
+      if (e > 1) t += 2.0 * (double)e * (double)M * (double)N * 4.0 / 5.0e12;
       if (t < best * 0.999) {
         best = t;
         se = e;
@@ -377,15 +378,18 @@ static hipError_t launch_nf4_forward_stream(const float* a, const float* scales,
     }
   }
   float* dst = c;
+  uint32_t* counters = nullptr;
+  // the kernel sums its own chunk partials (per-strip arrival counters; 32-bit byte offsets)
+  const bool fused = se > 1 && strips <= kWsCounters && (uint64_t)se * (uint64_t)M * (uint64_t)N * 4 < (1ull << 32);
   if (se > 1) {
     hipError_t e = stream_workspace(stream, (size_t)se * (size_t)M * (size_t)N * sizeof(float),
-                                    reinterpret_cast<void**>(&dst));
+                                    reinterpret_cast<void**>(&dst), fused ? &counters : nullptr);
     if (e != hipSuccess) return e;
   }
-  hipError_t e = launch_forward_stream((int)(strips * se), a, scales, reinterpret_cast<const uint32_t*>(codes), dst,
-                                       (int)M, (int)N, (int)K, (int)chunk, (int)strips, stream);
+  hipError_t e = launch_forward_stream((int)(strips * se), a, scales, reinterpret_cast<const uint32_t*>(codes), dst, c,
+                                       counters, (int)M, (int)N, (int)K, (int)chunk, (int)strips, (int)se, stream);
   if (e != hipSuccess) return e;
-  if (se > 1) {
+  if (se > 1 && !fused) {
     const int64_t n4 = M * N / 4;
     e = launch_grad_a_reduce((int)std::min<int64_t>(cdiv(n4, 256), 8192), dst, c, n4, (int)se, stream);
   }

@@ -108,6 +108,49 @@ def test_forward_deterministic(lib):
         assert np.array_equal(r1.view(np.uint32), r2.view(np.uint32))
 
 
+@pytest.mark.parametrize("M,N,K,splits", [(16, 2048, 1536, 4), (3, 520, 1344, 5), (1, 18944, 3584, 3),
+                                          (16, 3584, 18944, 17), (8, 256, 8192, 64)])
+def test_forward_stream_split_sum_is_chunk_partials_in_order(lib, M, N, K, splits):
+    """The streaming forward's chunk sum, done by each strip's last workgroup to finish, equals bit for bit
+    the unsplit kernel run on each K-chunk alone, summed on the host in fp32 in chunk order."""
+    a, s, b = fwd_inputs(M, N, K, seed=5 * M + N + K + splits)
+    chunk = -(-(-(-K // splits)) // 128) * 128
+    full = host(lib.forward(dev(a), dev(s), dev(b), splits=splits, kernel="stream"))
+    acc = None
+    for k0 in range(0, K, chunk):
+        k1 = min(K, k0 + chunk)
+        part = host(lib.forward(dev(a[:, k0:k1]), dev(s[:, k0 // 64:k1 // 64]), dev(b[:, k0 // 2:k1 // 2]),
+                                splits=1, kernel="stream"))
+        acc = part.copy() if acc is None else (acc + part).astype(np.float32)
+    assert -(-K // chunk) > 1
+    assert np.array_equal(full.view(np.uint32), acc.view(np.uint32))
+
+
+def test_forward_stream_split_counters_across_calls(lib):
+    """Split streaming calls of different strip and chunk counts back to back on one stream, interleaved with
+    backward split calls (all share the workspace's arrival counters): every output written in full (outputs
+    start as NaN), within the bound, and the second pass bitwise equal to the first."""
+    shapes = [(16, 2048, 1536, 4), (1, 520, 1344, 5), (8, 256, 8192, 64), (16, 4096, 512, 3)]
+    data = [fwd_inputs(M, N, K, seed=400 + i) for i, (M, N, K, _) in enumerate(shapes)]
+    devs = [(dev(a), dev(s), dev(b)) for a, s, b in data]
+    gb = dev(synth.grad_out_normal(16, 2048, seed=450))
+    firsts = []
+    for rnd in range(2):
+        outs = []
+        for (M, N, K, sp), d in zip(shapes, devs):
+            o = torch.full((M, N), float("nan"), device="cuda")
+            outs.append(lib.forward(*d, out=o, splits=sp, kernel="stream"))
+            lib.grad_a_forced(gb, devs[0][1], devs[0][2], "stream", rb=0, splits=5)
+        res = [host(o) for o in outs]
+        for i, ((M, N, K, sp), (a, s, b)) in enumerate(zip(shapes, data)):
+            if rnd == 0:
+                ref, S = oracle.forward(a, s, b, M, N, K)
+                assert np.all(np.abs(res[i].astype(np.float64) - ref) <= 2e-3 * S + 1e-6), f"shape {i}"
+                firsts.append(res[i])
+            else:
+                assert np.array_equal(res[i].view(np.uint32), firsts[i].view(np.uint32)), f"shape {i}"
+
+
 def test_forward_one_hot_rows_give_fp16_weight_columns(lib):
     M, N, K = 9, 136, 320
     b = synth.random_code_bytes(N, K, seed=93)
