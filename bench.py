@@ -125,10 +125,10 @@ def kernel_name_for(plan, N=None):
     return "grad_a_tile_kernel<%d>" % plan["rb"]
 
 
-# Device code of the grad_A kernels; a recorded counter summary is valid only
+# Device code of the dominant kernel (the fp16 fragment pass and the wide
+# kernel, with their shared headers); a recorded counter summary is valid only
 # for the sources it was taken on.
-KERNEL_SOURCES = ("nf4_grad_a.hip", "nf4_grad_a_wide.hip", "nf4_grad_a_skinny.hip", "nf4_kernel_util.h",
-                  "nf4_device.h")
+KERNEL_SOURCES = ("nf4_grad_a_wide.hip", "nf4_kernel_util.h", "nf4_device.h")
 
 
 def source_digest():
