@@ -345,10 +345,9 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
 // reduction is split into chunks of whole 64-wide stages (fp32 partials in the
 // stream's workspace, summed in chunk order by the reduce kernel).  splits <= 0
 // picks the count by the same cost model as the backward tiles.
-// Streaming forward (M <= 16): 128-column strips x K chunks of whole 128-wide
-// steps.  The chunk count comes from the same bandwidth model as the backward
-// streaming kernel (whole rounds of two workgroups per CU, partials and a
-// reduce launch per split); a split chunk keeps at least two steps.
+// Streaming forward (M <= 16): 256-column strips x K chunks of whole 128-wide
+// steps, the chunk partials summed inside the kernel by each strip's last
+// workgroup (the reduce kernel only past the counters' limits).
 static hipError_t launch_nf4_forward_stream(const float* a, const float* scales, const uint8_t* codes, float* c,
                                             int64_t M, int64_t N, int64_t K, int splits, hipStream_t stream) {
   const int64_t strips = forward_stream_strips(N);

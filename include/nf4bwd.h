@@ -41,9 +41,12 @@
  *     share it (they run in order); concurrent calls on different streams
  *     use different buffers and are safe.  Calls on one stream must be issued
  *     from one host thread at a time (a call that grows the buffer frees the
- *     old one in stream order, before work another thread enqueues later).  A stream handle that is destroyed
- *     while its calls are still running must not be reused by a new stream
- *     before they finish (the new stream would inherit the buffer).
+ *     old one in stream order, before work another thread enqueues later).
+ *     A stream handle that is destroyed while its calls are still running
+ *     must not be reused by a new stream before they finish (the new stream
+ *     would inherit the buffer).  The buffer starts with per-strip arrival
+ *     counters, zeroed when it is allocated; the streaming kernels count
+ *     their split workgroups on them and leave them at zero.
  */
 #ifndef NF4BWD_H
 #define NF4BWD_H
@@ -188,7 +191,7 @@ int nf4_grad_a_grouped(const nf4_grad_a_problem* problems, int count, int64_t M,
  *   K % 64 == 0 and N % 8 == 0 (NF4_ERR_SHAPE otherwise), and a, codes below
  *   2 GiB.  M == 0 or N == 0 enqueues nothing; K == 0 writes zeros.  Bitwise
  *   deterministic for a given (M, N, K).  1 <= M <= 16 runs a streaming
- *   kernel (64-column strips of C, the weight read once); larger M runs
+ *   kernel (256-column strips of C, the weight read once); larger M runs
  *   512 x 128 tiles.  Uses the stream's workspace (see the shared rules) for
  *   an fp16 copy of `a` (tiles: 2 * 16*ceil(M/16) * K bytes) and, when K is
  *   split, fp32 partials.
