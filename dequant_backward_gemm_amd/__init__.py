@@ -49,6 +49,14 @@ def _load() -> ctypes.CDLL:
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python dequant_backward_gemm_amd/build.py` "
             "(hipcc, gfx950). There is no CPU fallback.")
+    # One HIP runtime per process: PyTorch ships its own libamdhip64, and the
+    # library must bind to that copy, since it works on torch's memory and
+    # streams.  Loaded first, the library would pull in the system runtime,
+    # and every launch on torch's memory would then fail.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.nf4_grad_a.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
