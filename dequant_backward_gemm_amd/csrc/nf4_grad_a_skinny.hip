@@ -43,13 +43,13 @@ constexpr int kSkWaveBytes = kSkTabBytes + 1024;      // + A staging
 constexpr int kSkRedBytes = kSkinnyWaves * 16 * kSkinnyBK * 4;  // 64 KiB reduction buffer
 static_assert(kSkinnyWaves * kSkWaveBytes <= kSkRedBytes, "loop LDS fits in the reduction buffer");
 
+// One workgroup's strip and N-chunk: logical index `logical` of the
+// problem's tiles_k x splits workgroups (strip fastest).
 template <bool VEC_A>
-__global__ __launch_bounds__(512, 2) void grad_a_stream_kernel(const float* __restrict__ G,
-                                                               const float* __restrict__ S,
-                                                               const uint32_t* __restrict__ C32,
-                                                               float* out, float* __restrict__ grad_a,
-                                                               uint32_t* __restrict__ counters, int M, int N, int K,
-                                                               int n_chunk, int tiles_k, int splits) {
+__device__ __forceinline__ void stream_strip(const float* __restrict__ G, const float* __restrict__ S,
+                                             const uint32_t* __restrict__ C32, float* out, float* __restrict__ grad_a,
+                                             uint32_t* __restrict__ counters, int M, int N, int K, int n_chunk,
+                                             int tiles_k, int splits, int logical) {
   __shared__ __attribute__((aligned(16))) uint32_t smem[kSkRedBytes / 4];
   __shared__ uint32_t last_in_strip;
 
@@ -58,7 +58,6 @@ __global__ __launch_bounds__(512, 2) void grad_a_stream_kernel(const float* __re
   const int lane = tid & 63;
   const int ci = lane & 15, q = lane >> 4;
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = logical % tiles_k;
   const int split = logical / tiles_k;
   const int k0 = kt * kSkinnyBK;
@@ -265,9 +264,42 @@ __global__ __launch_bounds__(512, 2) void grad_a_stream_kernel(const float* __re
   }
 }
 
+template <bool VEC_A>
+__global__ __launch_bounds__(512, 2) void grad_a_stream_kernel(const float* __restrict__ G,
+                                                               const float* __restrict__ S,
+                                                               const uint32_t* __restrict__ C32,
+                                                               float* out, float* __restrict__ grad_a,
+                                                               uint32_t* __restrict__ counters, int M, int N, int K,
+                                                               int n_chunk, int tiles_k, int splits) {
+  stream_strip<VEC_A>(G, S, C32, out, grad_a, counters, M, N, K, n_chunk, tiles_k, splits,
+                      xcd_remap(blockIdx.x, gridDim.x));
+}
+
+// Several problems sharing M in one grid, each with the workgroups (and the
+// N-chunks) its own launch would have, so each result is bitwise the one its
+// own launch gives.  Problem p owns blocks [begin, begin + padded): its
+// workgroup count rounded up to a multiple of 8, so that its blocks start on
+// XCD 0 and the same XCD remap as a launch of its own applies inside it; the
+// padding blocks exit at once.
+__global__ __launch_bounds__(512, 2) void grad_a_stream_grouped_kernel(StreamGroup g) {
+  int p = 0;
+  while (p + 1 < g.count && (int)blockIdx.x >= g.p[p + 1].begin) ++p;
+  const StreamProblem& w = g.p[p];
+  const int local = (int)blockIdx.x - w.begin;
+  const int logical = xcd_remap(local, w.padded);
+  if (logical >= w.tiles_k * w.splits) return;
+  stream_strip<true>(w.G, w.S, w.C32, w.part, w.grad_a, w.counters, g.M, w.N, w.K, w.n_chunk, w.tiles_k, w.splits,
+                     logical);
+}
+
 bool stream_kernel_supported(int64_t M, int64_t N, int64_t K) {
   return M >= 1 && M <= 16 && N > 0 && (uint64_t)M * (uint64_t)N * 4 < (1ull << 31) &&
          (uint64_t)N * (uint64_t)K / 2 < (1ull << 31);
+}
+
+hipError_t launch_grad_a_stream_grouped(const StreamGroup& g, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(grad_a_stream_grouped_kernel, dim3(grid), dim3(512), 0, stream, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_grad_a_stream(int grid, const float* grad_out, const float* scales, const uint32_t* codes,

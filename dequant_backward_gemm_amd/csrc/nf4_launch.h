@@ -145,6 +145,29 @@ hipError_t launch_nf4_forward(const float* a, const float* scales, const uint8_t
 // 32-bit byte offsets.
 constexpr int kStreamBK = 128;
 bool stream_kernel_supported(int64_t M, int64_t N, int64_t K);
+// Grouped launch of the streaming kernel (nf4_grad_a_skinny.hip): problems
+// sharing M, each with its own plan's strips and N-chunks (bitwise the result
+// of its own launch).  Problem p owns blocks [begin, begin + padded), padded =
+// its workgroup count rounded up to a multiple of 8; part = its split
+// partials (grad_a itself when splits == 1), counters = its strips' arrival
+// counters (null when splits == 1).  Requires N % 4 == 0.
+constexpr int kStreamGroupMax = 8;
+struct StreamProblem {
+  const float* G;
+  const float* S;
+  const uint32_t* C32;
+  float* part;
+  float* grad_a;
+  uint32_t* counters;
+  int N, K, n_chunk, tiles_k, splits, begin, padded;
+};
+struct StreamGroup {
+  StreamProblem p[kStreamGroupMax];
+  int count;
+  int M;
+};
+hipError_t launch_grad_a_stream_grouped(const StreamGroup& g, int grid, hipStream_t stream);
+
 // With splits > 1, dst holds the splits' partials and, when `counters` (one
 // per strip, zero on entry and on exit) is given, the last workgroup of each
 // strip to finish sums them in split order into grad_a; without counters the

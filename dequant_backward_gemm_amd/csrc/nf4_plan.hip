@@ -439,14 +439,94 @@ hipError_t launch_nf4_forward(const float* a, const float* scales, const uint8_t
   return e;
 }
 
+// Grouped streaming launch (M <= 16): the problems nf4_grad_a would run on
+// the streaming kernel with its split sum inside the kernel (N % 4 == 0, the
+// counters and offsets within their limits) run as one grid, each with its
+// own plan's workgroups, so each result is bitwise that of its own call; the
+// others run through their own plans.  Problems are ordered by workgroup size
+// (N-chunk), largest first, so the long workgroups start first.
+static hipError_t launch_grad_a_grouped_stream(const float* const* grad_out, const float* const* scales,
+                                               const uint8_t* const* codes, float* const* grad_a, const int64_t* N,
+                                               const int64_t* K, int count, int64_t M, hipStream_t stream) {
+  int idx[kStreamGroupMax];
+  GradAPlan plans[kStreamGroupMax];
+  int ng = 0;
+  int64_t strips_split = 0;  // counters the split problems need
+  for (int i = 0; i < count; ++i) {
+    if (K[i] == 0) continue;
+    const GradAPlan pl = plan_grad_a(M, N[i], K[i]);
+    const int64_t tk = cdiv(K[i], kStreamBK);
+    const bool fits = pl.kernel == 4 && (N[i] % 4) == 0 && ng < kStreamGroupMax &&
+                      (pl.splits == 1 || ((uint64_t)pl.splits * (uint64_t)M * (uint64_t)K[i] * 4 < (1ull << 32) &&
+                                          strips_split + tk <= kWsCounters));
+    if (fits) {
+      plans[ng] = pl;
+      idx[ng++] = i;
+      if (pl.splits > 1) strips_split += tk;
+    } else {
+      hipError_t e = launch_grad_a(grad_out[i], scales[i], codes[i], grad_a[i], M, N[i], K[i], stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  if (ng == 0) return hipSuccess;
+  int order[kStreamGroupMax];
+  for (int j = 0; j < ng; ++j) order[j] = j;
+  std::stable_sort(order, order + ng, [&](int a, int b) { return plans[a].n_chunk > plans[b].n_chunk; });
+  size_t off[kStreamGroupMax], total_bytes = 0;
+  for (int j = 0; j < ng; ++j) {
+    const GradAPlan& pl = plans[order[j]];
+    off[j] = total_bytes;
+    if (pl.splits > 1)
+      total_bytes += ((size_t)pl.splits * (size_t)M * (size_t)K[idx[order[j]]] * sizeof(float) + 255) & ~(size_t)255;
+  }
+  char* base = nullptr;
+  uint32_t* counters = nullptr;
+  hipError_t e = stream_workspace(stream, std::max<size_t>(total_bytes, 256), reinterpret_cast<void**>(&base),
+                                  &counters);
+  if (e != hipSuccess) return e;
+  StreamGroup g{};
+  g.count = ng;
+  g.M = (int)M;
+  int begin = 0;
+  int cbase = 0;
+  for (int j = 0; j < ng; ++j) {
+    const int i = idx[order[j]];
+    const GradAPlan& pl = plans[order[j]];
+    StreamProblem& w = g.p[j];
+    w.G = grad_out[i];
+    w.S = scales[i];
+    w.C32 = reinterpret_cast<const uint32_t*>(codes[i]);
+    w.grad_a = grad_a[i];
+    w.N = (int)N[i];
+    w.K = (int)K[i];
+    w.n_chunk = pl.n_chunk;
+    w.tiles_k = (int)cdiv(K[i], kStreamBK);
+    w.splits = pl.splits;
+    if (pl.splits > 1) {
+      w.part = reinterpret_cast<float*>(base + off[j]);
+      w.counters = counters + cbase;
+      cbase += w.tiles_k;
+    } else {
+      w.part = grad_a[i];
+      w.counters = nullptr;
+    }
+    w.begin = begin;
+    w.padded = (int)cdiv(pl.grid, 8) * 8;
+    begin += w.padded;
+  }
+  return launch_grad_a_stream_grouped(g, begin, stream);
+}
+
 // Grouped grad_A: problems the fragment-fed wide kernel takes (M > 16, N % 64
 // == 0, operands below 2 GiB) run as one grid, longest reduction first;
-// every other problem runs through its own nf4_grad_a plan.  Each grouped
+// M <= 16 problems run as one grid of the streaming kernel (above); every
+// other problem runs through its own nf4_grad_a plan.  Each grouped wide
 // problem's grad_out goes through its own fragment pass first (the fragments
 // of all of them share the stream's workspace).
 hipError_t launch_grad_a_grouped(const float* const* grad_out, const float* const* scales,
                                  const uint8_t* const* codes, float* const* grad_a, const int64_t* N,
                                  const int64_t* K, int count, int64_t M, hipStream_t stream) {
+  if (M <= 16) return launch_grad_a_grouped_stream(grad_out, scales, codes, grad_a, N, K, count, M, stream);
   int idx[kWideGroupMax];
   int ng = 0;
   for (int i = 0; i < count; ++i) {

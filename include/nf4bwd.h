@@ -151,19 +151,21 @@ int nf4_grad_a_forced(const float* grad_out, const float* scales, const uint8_t*
 
 /*
  * nf4_grad_a_grouped -- up to NF4_GROUP_MAX grad_A problems that share M (for
- * example a layer's projections) in as few launches as possible: every
- * problem the large-M wide kernel takes (M > 16, N % 64 == 0, grad_out and
+ * example a layer's projections) in as few launches as possible.  For M > 16,
+ * every problem the large-M wide kernel takes (N % 64 == 0, grad_out and
  * codes below 2 GiB) runs in one grid, the tiles of the longest reductions
  * first, which keeps the CUs busy where separate launches end in a part-full
- * round; any other problem runs as nf4_grad_a would run it.  Each problem's
- * fields mean what nf4_grad_a's arguments mean, with the same layout,
- * ownership and bound; results are bitwise equal to nf4_grad_a_forced with
- * kernel 5 and one N-chunk for the grouped problems, and to nf4_grad_a for the
- * others.  The grad_a arrays must not alias each other or any input.  The
- * fp16 fragments of all grouped grad_outs share the stream's workspace
- * (sum of 2 * 16*ceil(M/16) * N bytes).  NF4_ERR_SHAPE if count is outside
- * 0..NF4_GROUP_MAX or a problem's shape is invalid; nothing is enqueued on
- * any argument error.
+ * round; results are bitwise equal to nf4_grad_a_forced with kernel 5 and one
+ * N-chunk.  For M <= 16, every problem nf4_grad_a would run on the streaming
+ * kernel (N % 4 == 0) runs in one grid of that kernel with its own plan's
+ * strips and N-chunks, the largest chunks first; results are bitwise equal to
+ * nf4_grad_a.  Any other problem runs as nf4_grad_a would run it.  Each
+ * problem's fields mean what nf4_grad_a's arguments mean, with the same
+ * layout, ownership and bound.  The grad_a arrays must not alias each other
+ * or any input.  The fp16 fragments of all grouped grad_outs (M > 16: sum of
+ * 2 * 16*ceil(M/16) * N bytes) or the split partials (M <= 16) share the
+ * stream's workspace.  NF4_ERR_SHAPE if count is outside 0..NF4_GROUP_MAX or
+ * a problem's shape is invalid; nothing is enqueued on any argument error.
  */
 #define NF4_GROUP_MAX 8
 typedef struct nf4_grad_a_problem {

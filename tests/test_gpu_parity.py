@@ -259,6 +259,44 @@ def test_grad_a_grouped_matches_separate_calls(lib, M):
         assert_within_bound(gpu, ref, S, f"grouped {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_grad_a_grouped_skinny_matches_separate_calls(lib, M):
+    """M <= 16: the streaming problems run as one grid, each bitwise equal to its own nf4_grad_a call (split
+    and unsplit plans, N tails inside a k-step, K % 128 == 64); N % 4 != 0 and N == 0 problems run on their
+    own; every output within the bound.  Run twice: the second pass reuses the arrival counters."""
+    shapes = [(3000, 512), (700, 1344), (4100, 384), (102, 256), (2048, 640), (0, 128), (96, 64), (9000, 128)]
+    data = [random_inputs(M, N, K, seed=11 * M + N + K) for (N, K) in shapes]
+    devs = [(dev(g), dev(s), dev(b)) for g, s, b in data]
+    seps = [host(lib.grad_a(*d)) for d in devs]
+    for rnd in range(2):
+        outs = [torch.full((M, K), float("nan"), device="cuda") for (N, K) in shapes]
+        lib.grad_a_grouped(devs, outs=outs)
+        for (N, K), (g, s, b), o, sep in zip(shapes, data, outs, seps):
+            gpu = host(o)
+            assert np.array_equal(gpu.view(np.uint32), sep.view(np.uint32)), (rnd, M, N, K)
+            if rnd == 0:
+                ref, S = oracle.grad_a(g, s, b, M, N, K)
+                assert_within_bound(gpu, ref, S, f"grouped skinny {M}x{N}x{K}")
+
+
+def test_grad_a_grouped_skinny_layer_shapes(lib):
+    """A 7B-class layer's seven projections at M = 16 in one grouped call: bitwise equal to separate calls."""
+    M = 16
+    shapes = [(3584, 3584), (512, 3584), (512, 3584), (3584, 3584), (18944, 3584), (18944, 3584), (3584, 18944)]
+    devs = []
+    for i, (N, K) in enumerate(shapes):
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(500 + i)
+        g = torch.empty((M, N), device="cuda").normal_(0.0, 1.0, generator=gen)
+        sc = torch.empty((N, K // 64), device="cuda").uniform_(0.01, 0.1, generator=gen)
+        cd = torch.randint(0, 256, (N, K // 2), device="cuda", dtype=torch.uint8, generator=gen)
+        devs.append((g, sc, cd))
+    seps = [host(lib.grad_a(*d)) for d in devs]
+    outs = lib.grad_a_grouped(devs)
+    for (N, K), o, sep in zip(shapes, outs, seps):
+        assert np.array_equal(host(o).view(np.uint32), sep.view(np.uint32)), (N, K)
+
+
 def test_grad_a_grouped_edges(lib):
     g, s, b = random_inputs(40, 128, 256, seed=5)
     d = (dev(g), dev(s), dev(b))
