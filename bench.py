@@ -403,6 +403,55 @@ def per_config_aux(torch, nb, trials=5):
     return res
 
 
+def per_config_grouped_skinny(torch, nb, layers=3, trials=5):
+    """A 7B-class layer's seven projections at M in {1, 8, 16} (the skinny sweep's token counts): seven
+    nf4_grad_a calls against one nf4_grad_a_grouped call, per layer, weights rotated over `layers` layers so
+    the Infinity Cache does not hold them.  Algorithmic bytes as for grad_A (codes, scales, grad_out, grad_A)."""
+    shapes = [(n, k) for (_, n, k) in PROJ]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    W = [[(torch.empty((n, k // 64), device="cuda").uniform_(0.005, 0.05, generator=gen),
+           torch.randint(0, 256, (n, k // 2), device="cuda", dtype=torch.uint8, generator=gen)) for (n, k) in shapes]
+         for _ in range(layers)]
+    res = {}
+    for M in (1, 8, 16):
+        G = [torch.empty((M, n), device="cuda").normal_(0.0, 1.0, generator=gen) for (n, k) in shapes]
+        O = [torch.empty((M, k), device="cuda") for (n, k) in shapes]
+        by = sum(alg_bytes(M, n, k) for (n, k) in shapes)
+
+        def separate(l):
+            for i in range(len(shapes)):
+                nb.grad_a(G[i], W[l][i][0], W[l][i][1], out=O[i])
+
+        def grouped(l):
+            nb.grad_a_grouped([(G[i], W[l][i][0], W[l][i][1]) for i in range(len(shapes))], outs=O)
+
+        row = {"M": M, "layer_alg_bytes": by}
+        for name, fn in (("separate", separate), ("grouped", grouped)):
+            for l in range(layers):
+                fn(l)
+            torch.cuda.synchronize()
+            tt = []
+            for _ in range(trials):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for r in range(4):
+                    for l in range(layers):
+                        fn(l)
+                e1.record()
+                torch.cuda.synchronize()
+                tt.append(e0.elapsed_time(e1) * 1e-3 / (4 * layers))
+            tt.sort()
+            med = tt[len(tt) // 2]
+            row[name + "_us"] = round(med * 1e6, 2)
+            row[name + "_gbs"] = round(by / med / 1e9, 1)
+        log(f"[bench] skinny layer M={M}: separate {row['separate_us']:.1f} us, grouped {row['grouped_us']:.1f} us")
+        res[f"layer_m{M}"] = row
+    del W
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline_rms_norm(target_s=5.0):
     """The fp64 RMSNorm-backward oracle on the 8192 x 3584 shape, repeated until about `target_s` seconds."""
     import numpy as np
@@ -619,6 +668,7 @@ def main():
     per_config_fwd = None if args.no_configs else per_config_table(torch, nb, op="forward")
     per_config_rms = None if args.no_configs else per_config_rms_norm(torch, nb)
     per_config_aux_ = None if args.no_configs else per_config_aux(torch, nb)
+    grouped_skinny = None if args.no_configs else per_config_grouped_skinny(torch, nb)
     cpu = None if args.no_cpu else cpu_baseline()
 
     rec = {
@@ -652,6 +702,7 @@ def main():
         "per_config_forward": per_config_fwd,
         "per_config_rms_norm": per_config_rms,
         "per_config_aux": per_config_aux_,
+        "grouped_skinny_layer": grouped_skinny,
     }
     print(json.dumps(rec), flush=True)
 
