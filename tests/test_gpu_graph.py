@@ -1,0 +1,60 @@
+"""The library's calls inside a HIP graph (torch.cuda.CUDAGraph on the calls' stream): the streaming
+kernel's in-kernel split sum (arrival counters left at zero by every replay), the fragment pass and wide
+kernel, and the forward streaming kernel.  Each replay, with new input values copied in and eager calls
+on the same workspace between replays, is compared bitwise with an eager call on the same inputs.  The
+workspace is allocated by an eager call before capture, so nothing is allocated inside the graph."""
+
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _inputs(M, N, K, seed):
+    b = synth.random_code_bytes(N, K, seed)
+    s = synth.random_scales_uniform(N, K, seed + 1)
+    g = synth.grad_out_normal(M, N, seed + 2)
+    return [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (g, s, b)]
+
+
+def test_calls_in_a_graph_match_eager(lib):
+    st = torch.cuda.Stream()
+    cases = [("stream", 16, 3000, 512, 4), ("wide16", 600, 1024, 384, 1)]
+    with torch.cuda.stream(st):
+        ins = [_inputs(M, N, K, seed=600 + i) for i, (_, M, N, K, _) in enumerate(cases)]
+        outs = [torch.empty((M, K), device="cuda") for (_, M, N, K, _) in cases]
+        a_fwd = torch.randn((8, 1024), device="cuda")
+        w_fwd = _inputs(8, 2048, 1024, seed=650)[1:]
+        c_fwd = torch.empty((8, 2048), device="cuda")
+
+        def run():
+            for (kern, M, N, K, sp), (g, s, b), o in zip(cases, ins, outs):
+                lib.grad_a_forced(g, s, b, kern, rb=1 if kern == "wide16" else 0, splits=sp, out=o)
+            lib.forward(a_fwd, *w_fwd, out=c_fwd, splits=3, kernel="stream")
+
+        run()  # eager: allocates the stream's workspace before capture
+    st.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        run()
+    for rep in range(4):
+        with torch.cuda.stream(st):
+            for i, (_, M, N, K, _) in enumerate(cases):
+                fresh = _inputs(M, N, K, seed=700 + 10 * rep + i)
+                for dst, src in zip(ins[i], fresh):
+                    dst.copy_(src)
+            a_fwd.copy_(torch.randn((8, 1024), device="cuda"))
+        st.synchronize()
+        graph.replay()
+        st.synchronize()
+        got = [o.clone() for o in outs] + [c_fwd.clone()]
+        with torch.cuda.stream(st):
+            run()  # eager on the same inputs and workspace
+        st.synchronize()
+        want = outs + [c_fwd]
+        for k, (x, y) in enumerate(zip(got, want)):
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32)), (rep, k)
