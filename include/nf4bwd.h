@@ -47,6 +47,11 @@
  *     would inherit the buffer).  The buffer starts with per-strip arrival
  *     counters, zeroed when it is allocated; the streaming kernels count
  *     their split workgroups on them and leave them at zero.
+ *   - HIP graphs: the calls can be captured on a stream and replayed, as long
+ *     as the stream's workspace already holds what they need (an eager call
+ *     of the same shapes on that stream before capture); a capture that has
+ *     to grow the workspace would allocate inside the graph.  No call issues
+ *     hipMemset (buffers are cleared by kernels).
  */
 #ifndef NF4BWD_H
 #define NF4BWD_H
