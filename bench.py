@@ -162,6 +162,29 @@ def recorded_traffic():
         return None
 
 
+def device_clock_mhz(device=0):
+    """Peak shader clock the HIP runtime reports (hipDeviceAttributeClockRate, kHz) for the device, read
+    through the runtime copy this process already loaded (PyTorch's); None if it cannot be read."""
+    import ctypes
+    try:
+        path = None
+        with open("/proc/self/maps") as fh:
+            for line in fh:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            return None
+        hip = ctypes.CDLL(path)
+        v = ctypes.c_int(0)
+        hip_device_attribute_clock_rate = 5  # position of hipDeviceAttributeClockRate in hipDeviceAttribute_t
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), hip_device_attribute_clock_rate, device) != 0:
+            return None
+        return v.value / 1000.0
+    except OSError:
+        return None
+
+
 def copy_calibration(torch):
     """A plain device copy of known size, for scaling the HBM byte counters."""
     n = 256 << 20  # floats: 1 GiB
@@ -693,6 +716,7 @@ def main():
             "frac_of_roofline_time": round(step_roof * 1e3 / ms_per_step, 4),
             "device": props.name,
             "cus": props.multi_processor_count,
+            "peak_clock_mhz": device_clock_mhz(),
             "copy_gbs_measured": copy_gbs,
         },
         "roofline": roof,
