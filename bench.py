@@ -426,10 +426,11 @@ def per_config_aux(torch, nb, trials=5):
     return res
 
 
-def per_config_grouped_skinny(torch, nb, layers=3, trials=5):
+def per_config_grouped_skinny(torch, nb, layers=3, trials=5, op="grad_a"):
     """A 7B-class layer's seven projections at M in {1, 8, 16} (the skinny sweep's token counts): seven
-    nf4_grad_a calls against one nf4_grad_a_grouped call, per layer, weights rotated over `layers` layers so
-    the Infinity Cache does not hold them.  Algorithmic bytes as for grad_A (codes, scales, grad_out, grad_A)."""
+    nf4_grad_a calls against one nf4_grad_a_grouped call (op="forward": nf4_forward against
+    nf4_forward_grouped, activations [M, K]), per layer, weights rotated over `layers` layers so the Infinity
+    Cache does not hold them.  Algorithmic bytes: codes, scales, the fp32 input and output."""
     shapes = [(n, k) for (_, n, k) in PROJ]
     gen = torch.Generator(device="cuda")
     gen.manual_seed(11)
@@ -438,16 +439,24 @@ def per_config_grouped_skinny(torch, nb, layers=3, trials=5):
          for _ in range(layers)]
     res = {}
     for M in (1, 8, 16):
-        G = [torch.empty((M, n), device="cuda").normal_(0.0, 1.0, generator=gen) for (n, k) in shapes]
-        O = [torch.empty((M, k), device="cuda") for (n, k) in shapes]
+        fwd = op == "forward"
+        G = [torch.empty((M, k if fwd else n), device="cuda").normal_(0.0, 1.0, generator=gen) for (n, k) in shapes]
+        O = [torch.empty((M, n if fwd else k), device="cuda") for (n, k) in shapes]
         by = sum(alg_bytes(M, n, k) for (n, k) in shapes)
 
         def separate(l):
             for i in range(len(shapes)):
-                nb.grad_a(G[i], W[l][i][0], W[l][i][1], out=O[i])
+                if fwd:
+                    nb.forward(G[i], W[l][i][0], W[l][i][1], out=O[i])
+                else:
+                    nb.grad_a(G[i], W[l][i][0], W[l][i][1], out=O[i])
 
         def grouped(l):
-            nb.grad_a_grouped([(G[i], W[l][i][0], W[l][i][1]) for i in range(len(shapes))], outs=O)
+            probs = [(G[i], W[l][i][0], W[l][i][1]) for i in range(len(shapes))]
+            if fwd:
+                nb.forward_grouped(probs, outs=O)
+            else:
+                nb.grad_a_grouped(probs, outs=O)
 
         row = {"M": M, "layer_alg_bytes": by}
         for name, fn in (("separate", separate), ("grouped", grouped)):
@@ -468,7 +477,7 @@ def per_config_grouped_skinny(torch, nb, layers=3, trials=5):
             med = tt[len(tt) // 2]
             row[name + "_us"] = round(med * 1e6, 2)
             row[name + "_gbs"] = round(by / med / 1e9, 1)
-        log(f"[bench] skinny layer M={M}: separate {row['separate_us']:.1f} us, grouped {row['grouped_us']:.1f} us")
+        log(f"[bench] skinny layer {op} M={M}: separate {row['separate_us']:.1f} us, grouped {row['grouped_us']:.1f} us")
         res[f"layer_m{M}"] = row
     del W
     torch.cuda.empty_cache()
@@ -692,6 +701,7 @@ def main():
     per_config_rms = None if args.no_configs else per_config_rms_norm(torch, nb)
     per_config_aux_ = None if args.no_configs else per_config_aux(torch, nb)
     grouped_skinny = None if args.no_configs else per_config_grouped_skinny(torch, nb)
+    grouped_skinny_fwd = None if args.no_configs else per_config_grouped_skinny(torch, nb, op="forward")
     cpu = None if args.no_cpu else cpu_baseline()
 
     rec = {
@@ -727,6 +737,7 @@ def main():
         "per_config_rms_norm": per_config_rms,
         "per_config_aux": per_config_aux_,
         "grouped_skinny_layer": grouped_skinny,
+        "grouped_skinny_layer_forward": grouped_skinny_fwd,
     }
     print(json.dumps(rec), flush=True)
 

@@ -8,6 +8,7 @@ it is missing; there is no fallback of any kind.
     grad_a(grad_out, scales, codes)          -> fp32 [M, K]
     grad_a_grouped([(grad_out, scales, codes), ...])  -> [fp32 [M, K_i], ...]  (shared M, up to 8)
     forward(a, scales, codes)                -> fp32 [M, N]   (the same layer's forward product)
+    forward_grouped([(a, scales, codes), ...])  -> [fp32 [M, N_i], ...]  (shared M, up to 8)
     dequant(scales, codes, N, K)             -> fp32 [N, K]
     pack(w)                                  -> (scales fp32 [N, K/64], codes uint8 [N, K/2])
     rms_norm_backward(x, gamma, rms, dy)     -> (dx fp32 [rows, H], dgamma fp32 [H])
@@ -29,13 +30,18 @@ NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_HIP = 0, 1, 2, 3, 4
 
 EXPORTED_SYMBOLS = ("nf4_grad_a", "nf4_dequant", "nf4_pack", "nf4_status_string", "nf4_grad_a_plan",
                     "nf4_grad_a_forced", "nf4_release_workspaces", "nf4_forward", "nf4_forward_forced",
-                    "nf4_grad_a_grouped", "nf4_rms_norm_backward")
+                    "nf4_grad_a_grouped", "nf4_rms_norm_backward", "nf4_forward_grouped")
 GROUP_MAX = 8
 
 
 class _Problem(ctypes.Structure):
     _fields_ = [("grad_out", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("codes", ctypes.c_void_p),
                 ("grad_a", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class _ForwardProblem(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+                ("c", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
 
 
 class Nf4Error(RuntimeError):
@@ -76,6 +82,8 @@ def _load() -> ctypes.CDLL:
     lib.nf4_forward.restype = ctypes.c_int
     lib.nf4_forward_forced.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, vp]
     lib.nf4_forward_forced.restype = ctypes.c_int
+    lib.nf4_forward_grouped.argtypes = [vp, ci, i64, vp]
+    lib.nf4_forward_grouped.restype = ctypes.c_int
     lib.nf4_rms_norm_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, vp]
     lib.nf4_rms_norm_backward.restype = ctypes.c_int
     lib.nf4_grad_a_grouped.argtypes = [ctypes.c_void_p, ci, i64, vp]
@@ -225,6 +233,35 @@ def forward(a, scales, codes, out=None, stream=None, splits: int = 0, kernel: st
         st = _lib.nf4_forward(_ptr(a), _ptr(scales), _ptr(codes), _ptr(out), M, N, K, _stream_handle(stream))
     _check(st, "nf4_forward")
     return out
+
+
+def forward_grouped(problems, outs=None, stream=None):
+    """Forward products of several problems sharing M in as few launches as possible (M <= 16: one grid of the
+    streaming kernel, each result bitwise that of forward()).
+
+    problems: sequence of (a [M, K], scales [N, K/64], codes [N, K/2]); returns the list of c [M, N] tensors
+    (or fills `outs`)."""
+    import torch
+    if len(problems) > GROUP_MAX:
+        raise ValueError(f"at most {GROUP_MAX} problems per group")
+    arr = (_ForwardProblem * max(1, len(problems)))()
+    res = []
+    M = problems[0][0].shape[0] if problems else 0
+    for i, (a, s, c) in enumerate(problems):
+        Mi, K = a.shape
+        N = c.shape[0]
+        if Mi != M:
+            raise ValueError("all problems of a group share M")
+        _require(a, torch.float32, (M, K), "a")
+        _require(s, torch.float32, (N, K // 64), "scales")
+        _require(c, torch.uint8, (N, K // 2), "codes")
+        o = outs[i] if outs is not None else torch.empty((M, N), dtype=torch.float32, device=a.device)
+        _require(o, torch.float32, (M, N), "out")
+        arr[i] = _ForwardProblem(_ptr(a), _ptr(s), _ptr(c), _ptr(o), N, K)
+        res.append(o)
+    _check(_lib.nf4_forward_grouped(ctypes.cast(arr, ctypes.c_void_p), len(problems), M, _stream_handle(stream)),
+           "nf4_forward_grouped")
+    return res
 
 
 def rms_norm_backward(x, gamma, rms, dy, dx=None, dgamma=None, stream=None):

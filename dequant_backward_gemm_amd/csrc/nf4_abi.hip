@@ -131,6 +131,37 @@ int nf4_grad_a_grouped(const nf4_grad_a_problem* problems, int count, int64_t M,
   return from_hip(nf4::launch_grad_a_grouped(g, sc, cd, out, n, k, count, M, stream));
 }
 
+int nf4_forward_grouped(const nf4_forward_problem* problems, int count, int64_t M, hipStream_t stream) {
+  if (count < 0 || count > NF4_GROUP_MAX) return NF4_ERR_SHAPE;
+  if (count > 0 && problems == nullptr) return NF4_ERR_NULL;
+  if (M < 0) return NF4_ERR_SHAPE;
+  const float* a[NF4_GROUP_MAX];
+  const float* sc[NF4_GROUP_MAX];
+  const uint8_t* cd[NF4_GROUP_MAX];
+  float* out[NF4_GROUP_MAX];
+  int64_t n[NF4_GROUP_MAX], k[NF4_GROUP_MAX];
+  for (int i = 0; i < count; ++i) {
+    const nf4_forward_problem& p = problems[i];
+    const int64_t N = p.N, K = p.K;
+    if (!dims_ok(M, K) || !dims_ok(N, K) || !dims_ok(M, N) || (K % 64) != 0 || (N % 8) != 0) return NF4_ERR_SHAPE;
+    if (M > 0 && N > 0) {
+      if (p.c == nullptr) return NF4_ERR_NULL;
+      if (K > 0 && (p.a == nullptr || p.scales == nullptr || p.codes == nullptr)) return NF4_ERR_NULL;
+      if (!aligned16(p.c) || (K > 0 && (!aligned16(p.a) || !aligned16(p.scales) || !aligned16(p.codes))))
+        return NF4_ERR_ALIGN;
+      if (K > 0 && !nf4::forward_supported(M, N, K)) return NF4_ERR_SHAPE;
+    }
+    a[i] = p.a;
+    sc[i] = p.scales;
+    cd[i] = p.codes;
+    out[i] = p.c;
+    n[i] = N;
+    k[i] = K;
+  }
+  if (M == 0 || count == 0) return NF4_OK;
+  return from_hip(nf4::launch_nf4_forward_grouped(a, sc, cd, out, n, k, count, M, stream));
+}
+
 int nf4_rms_norm_backward(const float* x, const float* gamma, const float* rms, const float* dy, float* dx,
                           float* dgamma, int64_t rows, int64_t H, hipStream_t stream) {
   if (!dims_ok(rows, H) || !nf4::rms_norm_supported(rows, H)) return NF4_ERR_SHAPE;

@@ -53,13 +53,13 @@ constexpr int kFsCols = 16 * kFsTiles * kFsWaves;  // columns n of C per workgro
 constexpr int kFsTabBytes = 64;                   // per wave: the 16 fp32 levels
 constexpr int kFsABytes = 4 * 64 * 16;             // one step's A operands: [u][lane] x 16 B
 
+// One workgroup's strip and K-chunk: block `blk` of the problem's strips x
+// splits workgroups (strip fastest).
 template <int T>
-__global__ __launch_bounds__(512, 2) void nf4_forward_stream_kernel(const float* __restrict__ A,
-                                                                    const float* __restrict__ S,
-                                                                    const uint32_t* __restrict__ C32,
-                                                                    float* out, float* __restrict__ c,
-                                                                    uint32_t* __restrict__ counters, int M, int N,
-                                                                    int K, int k_chunk, int strips, int splits) {
+__device__ __forceinline__ void forward_strip(const float* __restrict__ A, const float* __restrict__ S,
+                                              const uint32_t* __restrict__ C32, float* out, float* __restrict__ c,
+                                              uint32_t* __restrict__ counters, int M, int N, int K, int k_chunk,
+                                              int strips, int splits, int blk) {
   __shared__ __attribute__((aligned(16))) uint32_t smem[(kFsWaves * kFsTabBytes + 2 * kFsABytes) / 4];
   __shared__ uint32_t last_in_strip;
 
@@ -68,8 +68,8 @@ __global__ __launch_bounds__(512, 2) void nf4_forward_stream_kernel(const float*
   const int lane = tid & 63;
   const int ci = lane & 15, q = lane >> 4;
 
-  const int strip = blockIdx.x % strips;
-  const int split = blockIdx.x / strips;
+  const int strip = blk % strips;
+  const int split = blk / strips;
   const int n0 = strip * (16 * T * kFsWaves) + 16 * T * wave;  // this wave's rows n0 .. n0 + 16T - 1
   const int kbeg = split * k_chunk;
   const int kend = min(K, kbeg + k_chunk);
@@ -257,6 +257,37 @@ __global__ __launch_bounds__(512, 2) void nf4_forward_stream_kernel(const float*
   }
   if (tid == 0) __hip_atomic_store(&counters[strip], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+template <int T>
+__global__ __launch_bounds__(512, 2) void nf4_forward_stream_kernel(const float* __restrict__ A,
+                                                                    const float* __restrict__ S,
+                                                                    const uint32_t* __restrict__ C32,
+                                                                    float* out, float* __restrict__ c,
+                                                                    uint32_t* __restrict__ counters, int M, int N,
+                                                                    int K, int k_chunk, int strips, int splits) {
+  forward_strip<T>(A, S, C32, out, c, counters, M, N, K, k_chunk, strips, splits, (int)blockIdx.x);
+}
+
+// Several problems sharing M in one grid, each with the workgroups (and the
+// K-chunks) its own launch would have, so each result is bitwise the one its
+// own launch gives.  Problem p owns blocks [begin, begin + padded), padded =
+// its workgroup count rounded up to a multiple of 8 (its blocks start on XCD
+// 0, as in a launch of its own); the padding blocks exit at once.
+__global__ __launch_bounds__(512, 2) void nf4_forward_stream_grouped_kernel(ForwardStreamGroup g) {
+  int p = 0;
+  while (p + 1 < g.count && (int)blockIdx.x >= g.p[p + 1].begin) ++p;
+  const ForwardStreamProblem& w = g.p[p];
+  const int blk = (int)blockIdx.x - w.begin;
+  if (blk >= w.strips * w.splits) return;
+  forward_strip<kFsTiles>(w.A, w.S, w.C32, w.part, w.c, w.counters, g.M, w.N, w.K, w.k_chunk, w.strips, w.splits,
+                          blk);
+}
+
+hipError_t launch_forward_stream_grouped(const ForwardStreamGroup& g, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(nf4_forward_stream_grouped_kernel, dim3(grid), dim3(512), 0, stream, g);
+  return hipGetLastError();
+}
+
 
 bool forward_stream_supported(int64_t M, int64_t N, int64_t K) {
   return M >= 1 && M <= 16 && N > 0 && (N % 8) == 0 && K > 0 && (K % 64) == 0 &&

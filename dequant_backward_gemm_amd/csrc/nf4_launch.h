@@ -140,6 +140,34 @@ constexpr int kForwardAuto = -1, kForwardTile = 0, kForwardStream = 1;
 hipError_t launch_nf4_forward(const float* a, const float* scales, const uint8_t* codes, float* c, int64_t M,
                               int64_t N, int64_t K, int kernel, int splits, hipStream_t stream);
 
+// Grouped launch of the streaming forward kernel: problems sharing M, each
+// with its own plan's strips and K-chunks (bitwise the result of its own
+// launch).  Problem p owns blocks [begin, begin + padded), padded = strips x
+// splits rounded up to a multiple of 8; part = its chunk partials (c itself
+// when splits == 1), counters = its strips' arrival counters (null when
+// splits == 1).
+constexpr int kStreamGroupMax = 8;  // problems per grouped streaming launch
+struct ForwardStreamProblem {
+  const float* A;
+  const float* S;
+  const uint32_t* C32;
+  float* part;
+  float* c;
+  uint32_t* counters;
+  int N, K, k_chunk, strips, splits, begin, padded;
+};
+struct ForwardStreamGroup {
+  ForwardStreamProblem p[kStreamGroupMax];
+  int count;
+  int M;
+};
+hipError_t launch_forward_stream_grouped(const ForwardStreamGroup& g, int grid, hipStream_t stream);
+// Grouped forward: M <= 16 problems on the streaming kernel in one grid, the
+// others through their own nf4_forward plans.
+hipError_t launch_nf4_forward_grouped(const float* const* a, const float* const* scales, const uint8_t* const* codes,
+                                      float* const* c, const int64_t* N, const int64_t* K, int count, int64_t M,
+                                      hipStream_t stream);
+
 // Streaming kernel for M <= 16 (nf4_grad_a_skinny.hip): 128-column strips,
 // N-chunks of whole 32-row k-steps, two 8-wave workgroups per CU; needs
 // 32-bit byte offsets.
@@ -151,7 +179,6 @@ bool stream_kernel_supported(int64_t M, int64_t N, int64_t K);
 // its workgroup count rounded up to a multiple of 8; part = its split
 // partials (grad_a itself when splits == 1), counters = its strips' arrival
 // counters (null when splits == 1).  Requires N % 4 == 0.
-constexpr int kStreamGroupMax = 8;
 struct StreamProblem {
   const float* G;
   const float* S;

@@ -348,8 +348,8 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
 // Streaming forward (M <= 16): 256-column strips x K chunks of whole 128-wide
 // steps, the chunk partials summed inside the kernel by each strip's last
 // workgroup (the reduce kernel only past the counters' limits).
-static hipError_t launch_nf4_forward_stream(const float* a, const float* scales, const uint8_t* codes, float* c,
-                                            int64_t M, int64_t N, int64_t K, int splits, hipStream_t stream) {
+// K chunking of the streaming forward: `splits` forced (> 0) or chosen.
+static void forward_stream_chunks(int64_t M, int64_t N, int64_t K, int splits, int64_t* se_out, int64_t* chunk_out) {
   const int64_t strips = forward_stream_strips(N);
   int64_t se = 1, chunk = K;
   if (splits > 0) {
@@ -376,10 +376,23 @@ static hipError_t launch_nf4_forward_stream(const float* a, const float* scales,
       }
     }
   }
+  *se_out = se;
+  *chunk_out = chunk;
+}
+
+// the kernel sums its own chunk partials (per-strip arrival counters; 32-bit byte offsets)
+static bool forward_stream_fused(int64_t M, int64_t N, int64_t se) {
+  return se > 1 && forward_stream_strips(N) <= kWsCounters && (uint64_t)se * (uint64_t)M * (uint64_t)N * 4 < (1ull << 32);
+}
+
+static hipError_t launch_nf4_forward_stream(const float* a, const float* scales, const uint8_t* codes, float* c,
+                                            int64_t M, int64_t N, int64_t K, int splits, hipStream_t stream) {
+  const int64_t strips = forward_stream_strips(N);
+  int64_t se = 1, chunk = K;
+  forward_stream_chunks(M, N, K, splits, &se, &chunk);
   float* dst = c;
   uint32_t* counters = nullptr;
-  // the kernel sums its own chunk partials (per-strip arrival counters; 32-bit byte offsets)
-  const bool fused = se > 1 && strips <= kWsCounters && (uint64_t)se * (uint64_t)M * (uint64_t)N * 4 < (1ull << 32);
+  const bool fused = forward_stream_fused(M, N, se);
   if (se > 1) {
     hipError_t e = stream_workspace(stream, (size_t)se * (size_t)M * (size_t)N * sizeof(float),
                                     reinterpret_cast<void**>(&dst), fused ? &counters : nullptr);
@@ -571,6 +584,84 @@ hipError_t launch_grad_a_grouped(const float* const* grad_out, const float* cons
   }
   g.total = begin;
   return launch_grad_a_wide_grouped(g, stream);
+}
+
+// Grouped forward (M <= 16): every problem nf4_forward would run on the
+// streaming kernel with its chunk sum inside the kernel runs in one grid, each
+// with its own plan's strips and K-chunks (bitwise the result of its own
+// call), largest chunk first; the others run through their own plans.
+hipError_t launch_nf4_forward_grouped(const float* const* a, const float* const* scales, const uint8_t* const* codes,
+                                      float* const* c, const int64_t* N, const int64_t* K, int count, int64_t M,
+                                      hipStream_t stream) {
+  int idx[kStreamGroupMax];
+  int64_t se_of[kStreamGroupMax], chunk_of[kStreamGroupMax];
+  int ng = 0;
+  int64_t strips_split = 0;
+  for (int i = 0; i < count; ++i) {
+    if (N[i] == 0) continue;
+    bool grouped = false;
+    if (M <= 16 && K[i] > 0 && forward_stream_supported(M, N[i], K[i]) && ng < kStreamGroupMax) {
+      int64_t se = 1, chunk = K[i];
+      forward_stream_chunks(M, N[i], K[i], 0, &se, &chunk);
+      const int64_t strips = forward_stream_strips(N[i]);
+      if (se == 1 || (forward_stream_fused(M, N[i], se) && strips_split + strips <= kWsCounters)) {
+        grouped = true;
+        se_of[ng] = se;
+        chunk_of[ng] = chunk;
+        idx[ng++] = i;
+        if (se > 1) strips_split += strips;
+      }
+    }
+    if (!grouped) {
+      hipError_t e = launch_nf4_forward(a[i], scales[i], codes[i], c[i], M, N[i], K[i], kForwardAuto, 0, stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  if (ng == 0) return hipSuccess;
+  int order[kStreamGroupMax];
+  for (int j = 0; j < ng; ++j) order[j] = j;
+  std::stable_sort(order, order + ng, [&](int x, int y) { return chunk_of[x] > chunk_of[y]; });
+  size_t off[kStreamGroupMax], total_bytes = 0;
+  for (int j = 0; j < ng; ++j) {
+    const int o = order[j];
+    off[j] = total_bytes;
+    if (se_of[o] > 1)
+      total_bytes += ((size_t)se_of[o] * (size_t)M * (size_t)N[idx[o]] * sizeof(float) + 255) & ~(size_t)255;
+  }
+  char* base = nullptr;
+  uint32_t* counters = nullptr;
+  hipError_t e = stream_workspace(stream, std::max<size_t>(total_bytes, 256), reinterpret_cast<void**>(&base),
+                                  &counters);
+  if (e != hipSuccess) return e;
+  ForwardStreamGroup g{};
+  g.count = ng;
+  g.M = (int)M;
+  int begin = 0, cbase = 0;
+  for (int j = 0; j < ng; ++j) {
+    const int o = order[j], i = idx[o];
+    ForwardStreamProblem& w = g.p[j];
+    w.A = a[i];
+    w.S = scales[i];
+    w.C32 = reinterpret_cast<const uint32_t*>(codes[i]);
+    w.c = c[i];
+    w.N = (int)N[i];
+    w.K = (int)K[i];
+    w.k_chunk = (int)chunk_of[o];
+    w.strips = forward_stream_strips(N[i]);
+    w.splits = (int)se_of[o];
+    if (w.splits > 1) {
+      w.part = reinterpret_cast<float*>(base + off[j]);
+      w.counters = counters + cbase;
+      cbase += w.strips;
+    } else {
+      w.part = c[i];
+      w.counters = nullptr;
+    }
+    w.begin = begin;
+    w.padded = (int)cdiv((int64_t)w.strips * w.splits, 8) * 8;
+    begin += w.padded;
+  }
+  return launch_forward_stream_grouped(g, begin, stream);
 }
 
 }  // namespace nf4

@@ -207,6 +207,30 @@ int nf4_forward(const float* a, const float* scales, const uint8_t* codes, float
                 int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /*
+ * nf4_forward_grouped -- up to NF4_GROUP_MAX forward products that share M
+ * (for example a layer's projections at decode size) in as few launches as
+ * possible: for 1 <= M <= 16, every problem nf4_forward would run on its
+ * streaming kernel runs in one grid of that kernel, each with its own plan's
+ * strips and K-chunks, the largest chunks first; results are bitwise equal to
+ * nf4_forward.  Any other problem (larger M, or limits of the in-kernel chunk
+ * sum) runs as nf4_forward would run it.  Each problem's fields mean what
+ * nf4_forward's arguments mean, with the same layout, ownership, requirements
+ * and bound; the c arrays must not alias each other or any input.  The chunk
+ * partials share the stream's workspace.  NF4_ERR_SHAPE if count is outside
+ * 0..NF4_GROUP_MAX or a problem's shape is invalid; nothing is enqueued on
+ * any argument error.
+ */
+typedef struct nf4_forward_problem {
+  const float* a;         /* [M][K] */
+  const float* scales;    /* [N][K/64] */
+  const uint8_t* codes;   /* [N][K/2] */
+  float* c;               /* [M][N], overwritten */
+  int64_t N;
+  int64_t K;
+} nf4_forward_problem;
+int nf4_forward_grouped(const nf4_forward_problem* problems, int count, int64_t M, hipStream_t stream);
+
+/*
  * nf4_forward_forced -- nf4_forward with the kernel and the number of K
  * chunks forced, for tests and tuning: kernel NF4_FORWARD_TILE (512 x 128
  * tiles, any M) or NF4_FORWARD_STREAM (the streaming kernel nf4_forward picks

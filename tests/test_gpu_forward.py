@@ -296,3 +296,40 @@ def test_forward_stream_rejects_large_m(lib):
     b = dev(np.zeros((8, 32), dtype=np.uint8))
     with pytest.raises(lib.Nf4Error):
         lib.forward(a, s, b, splits=1, kernel="stream")
+
+
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_forward_grouped_matches_separate_calls(lib, M):
+    """M <= 16: the streaming problems of a group run as one grid, each bitwise equal to its own nf4_forward
+    call (split and unsplit chunk plans, K % 128 == 64); N == 0 and K == 0 problems keep their contracts;
+    every output within the bound.  Run twice: the second pass reuses the arrival counters."""
+    shapes = [(2048, 1536), (520, 1344), (4096, 384), (96, 64), (0, 128), (256, 0), (18944, 3584), (3584, 18944)]
+    data = [fwd_inputs(M, N, K, seed=13 * M + N + K) for (N, K) in shapes]
+    devs = [(dev(a), dev(s), dev(b)) for a, s, b in data]
+    seps = [host(lib.forward(*d)) for d in devs]
+    for rnd in range(2):
+        outs = [torch.full((M, N), float("nan"), device="cuda") for (N, K) in shapes]
+        lib.forward_grouped(devs, outs=outs)
+        for (N, K), (a, s, b), o, sep in zip(shapes, data, outs, seps):
+            gpu = host(o)
+            assert np.array_equal(gpu.view(np.uint32), sep.view(np.uint32)), (rnd, M, N, K)
+            if rnd == 0 and N * K <= 4096 * 1536:
+                ref, S = oracle.forward(a, s, b, M, N, K)
+                assert np.all(np.abs(gpu.astype(np.float64) - ref) <= 2e-3 * S + 1e-6), (M, N, K)
+
+
+def test_forward_grouped_large_m_and_errors(lib):
+    """M > 16 problems run as nf4_forward runs them; more than 8 problems and mixed M are rejected."""
+    M = 40
+    shapes = [(256, 512), (136, 320)]
+    data = [fwd_inputs(M, N, K, seed=70 + N) for (N, K) in shapes]
+    devs = [(dev(a), dev(s), dev(b)) for a, s, b in data]
+    outs = lib.forward_grouped(devs)
+    for d, o in zip(devs, outs):
+        assert np.array_equal(host(o).view(np.uint32), host(lib.forward(*d)).view(np.uint32))
+    assert lib.forward_grouped([]) == []
+    with pytest.raises(ValueError):
+        lib.forward_grouped([devs[0]] * 9)
+    a2 = dev(synth.grad_out_normal(8, 512, seed=1))
+    with pytest.raises(ValueError):
+        lib.forward_grouped([devs[0], (a2, devs[0][1], devs[0][2])])
