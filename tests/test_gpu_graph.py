@@ -1,6 +1,6 @@
 """The library's calls inside a HIP graph (torch.cuda.CUDAGraph on the calls' stream): the streaming
 kernel's in-kernel split sum (arrival counters left at zero by every replay), the fragment pass and wide
-kernel, and the forward streaming kernel.  Each replay, with new input values copied in and eager calls
+kernel, the forward streaming kernel, and the grouped backward and forward launches at M <= 16.  Each replay, with new input values copied in and eager calls
 on the same workspace between replays, is compared bitwise with an eager call on the same inputs.  The
 workspace is allocated by an eager call before capture, so nothing is allocated inside the graph."""
 
@@ -31,10 +31,18 @@ def test_calls_in_a_graph_match_eager(lib):
         w_fwd = _inputs(8, 2048, 1024, seed=650)[1:]
         c_fwd = torch.empty((8, 2048), device="cuda")
 
+        grp = [_inputs(16, N, K, seed=660 + i) for i, (N, K) in enumerate([(3000, 512), (700, 1344), (9000, 128)])]
+        grp_out = [torch.empty((16, b.shape[1] * 2), device="cuda") for (g, s, b) in grp]
+        fgrp = [(torch.randn((8, K), device="cuda"),) + tuple(_inputs(8, N, K, seed=680 + i)[1:])
+                for i, (N, K) in enumerate([(2048, 1536), (520, 1344)])]
+        fgrp_out = [torch.empty((8, s.shape[0]), device="cuda") for (a, s, b) in fgrp]
+
         def run():
             for (kern, M, N, K, sp), (g, s, b), o in zip(cases, ins, outs):
                 lib.grad_a_forced(g, s, b, kern, rb=1 if kern == "wide16" else 0, splits=sp, out=o)
             lib.forward(a_fwd, *w_fwd, out=c_fwd, splits=3, kernel="stream")
+            lib.grad_a_grouped(grp, outs=grp_out)
+            lib.forward_grouped(fgrp, outs=fgrp_out)
 
         run()  # eager: allocates the stream's workspace before capture
     st.synchronize()
@@ -51,10 +59,10 @@ def test_calls_in_a_graph_match_eager(lib):
         st.synchronize()
         graph.replay()
         st.synchronize()
-        got = [o.clone() for o in outs] + [c_fwd.clone()]
+        got = [o.clone() for o in outs + [c_fwd] + grp_out + fgrp_out]
         with torch.cuda.stream(st):
             run()  # eager on the same inputs and workspace
         st.synchronize()
-        want = outs + [c_fwd]
+        want = outs + [c_fwd] + grp_out + fgrp_out
         for k, (x, y) in enumerate(zip(got, want)):
             assert torch.equal(x.view(torch.int32), y.view(torch.int32)), (rep, k)
