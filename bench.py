@@ -162,6 +162,28 @@ def recorded_traffic():
         return None
 
 
+def host_cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def numpy_blas():
+    """The BLAS numpy was built against (name and version), or None."""
+    try:
+        import numpy as np
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return f"{b.get('name')} {b.get('version')}"
+    except Exception:
+        return None
+
+
 def device_clock_mhz(device=0):
     """Peak shader clock the HIP runtime reports (hipDeviceAttributeClockRate, kHz) for the device, read
     through the runtime copy this process already loaded (PyTorch's); None if it cannot be read."""
@@ -540,7 +562,7 @@ def cpu_baseline(target_s=10.0, max_layers=8, op="grad_a"):
         cores = os.cpu_count()
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": min(cores, threads),
-            "kind": "oracle", "seconds": round(t, 2),
+            "kind": "oracle", "seconds": round(t, 2), "cpu_model": host_cpu_model(), "blas": numpy_blas(),
             "sample": f"{op}: {layers} layer(s) x the full step's 7 projections (q,k,v,o,gate,up,down) at {rows} "
                       f"of the 8192 token rows each: numpy fp64 dequant + matmul, {flops / 1e9:.1f} GFLOP"}
 
