@@ -21,7 +21,8 @@ the 256 MB Infinity Cache; `per_config_forward` the same layers' forward
 product and `per_config_rms_norm` the RMSNorm backward (algorithmic GB/s).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-configs]
-       python bench.py --forward-configs | --unfused-configs | --rmsnorm-configs | --aux-configs   (side tables)
+       python bench.py --forward-configs | --unfused-configs | --rmsnorm-configs | --aux-configs | --grouped-skinny
+                                                                                                   (side tables)
        python bench.py --one M,N,K [--steps K] [--warmup W]   (one shape, for counter collection)
        python bench.py --copy-calibration   (1 GiB device copy, for counter scaling)
 """
@@ -580,6 +581,8 @@ def main():
                     help="only the forward product's per-config table and its CPU oracle baseline (one JSON line)")
     ap.add_argument("--aux-configs", action="store_true",
                     help="only nf4_dequant and nf4_pack throughput on the full step's largest weight (one JSON line)")
+    ap.add_argument("--grouped-skinny", action="store_true",
+                    help="only the M <= 16 layer tables, separate against grouped, backward and forward (one JSON line)")
     ap.add_argument("--rmsnorm-configs", action="store_true",
                     help="only the RMSNorm backward's per-shape table and its CPU oracle baseline (one JSON line)")
     ap.add_argument("--one", type=str, default=None, metavar="M,N,K",
@@ -626,6 +629,11 @@ def main():
         return
     if args.aux_configs:
         print(json.dumps({"per_config_aux": per_config_aux(torch, nb)}), flush=True)
+        return
+    if args.grouped_skinny:
+        print(json.dumps({"grouped_skinny_layer": per_config_grouped_skinny(torch, nb),
+                          "grouped_skinny_layer_forward": per_config_grouped_skinny(torch, nb, op="forward")}),
+              flush=True)
         return
     if args.rmsnorm_configs:
         rec = {"per_config_rms_norm": per_config_rms_norm(torch, nb),
