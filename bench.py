@@ -529,6 +529,32 @@ def cpu_baseline_rms_norm(target_s=5.0):
             "sample": f"{reps} x the 8192 x 3584 RMSNorm backward (numpy fp64), algorithmic bytes / oracle time"}
 
 
+def cpu_baseline_configs(trials=3):
+    """The fp64 oracle on each parity configuration (tiny, attention projection, MLP pair, skinny sweep),
+    median of `trials` runs of dequant + matmul on the configuration's seeded inputs (generation excluded),
+    next to the GPU's median per-call time from the per-config table when given."""
+    import oracle
+    import synth
+    out = {}
+    plan = [("tiny", synth.CONFIGS["tiny"], 1.0), ("attn_proj", synth.CONFIGS["attn_proj"], 1e-2),
+            ("mlp_pair", synth.CONFIGS["mlp_pair"], 1e-2), ("skinny", synth.SKINNY_SHAPES, 1.0)]
+    for _, shapes, gstd in plan:
+        for i, shp in enumerate(shapes):
+            b = synth.random_code_bytes(shp.N, shp.K, 100 + i)
+            s = synth.random_scales_uniform(shp.N, shp.K, 101 + i)
+            g = synth.grad_out_normal(shp.M, shp.N, 102 + i, std=gstd)
+            tt = []
+            for _ in range(trials):
+                t0 = time.perf_counter()
+                oracle.grad_a(g, s, b, shp.M, shp.N, shp.K, with_bound=False)
+                tt.append(time.perf_counter() - t0)
+            tt.sort()
+            med = tt[len(tt) // 2]
+            out[shp.name] = {"oracle_s": round(med, 4),
+                             "oracle_tflops": round(2.0 * shp.M * shp.N * shp.K / med / 1e12, 6)}
+    return out
+
+
 def cpu_baseline(target_s=10.0, max_layers=8, op="grad_a"):
     """The fp64 oracle, as it stands, on a bounded sample of the full step: one layer's seven projections at
     3072 of the 8192 token rows each, repeated over further layers (fresh inputs) until about `target_s`
@@ -733,6 +759,12 @@ def main():
     grouped_skinny = None if args.no_configs else per_config_grouped_skinny(torch, nb)
     grouped_skinny_fwd = None if args.no_configs else per_config_grouped_skinny(torch, nb, op="forward")
     cpu = None if args.no_cpu else cpu_baseline()
+    if cpu is not None:
+        cpu["per_config"] = cpu_baseline_configs()
+        if per_config is not None:
+            for name, row in cpu["per_config"].items():
+                if name in per_config:
+                    row["gpu_speedup"] = round(row["oracle_s"] / (per_config[name]["us"] * 1e-6), 1)
 
     rec = {
         "metric": "NF4 grad_A GEMM TFLOP/s (2MNK/t) + % of MFMA or HBM roofline, per config",
