@@ -15,6 +15,8 @@ from oracle.nf4_oracle import (  # noqa: F401
     grad_a,
     grad_a_bruteforce,
     grad_a_fp16_operands,
+    grad_a_fp16_operands_from_weights,
+    grad_a_from_weights,
     num_k_blocks,
     pack,
     pack_codes,

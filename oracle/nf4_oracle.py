@@ -139,17 +139,28 @@ def grad_a(grad_out: np.ndarray, scales: np.ndarray, code_bytes: np.ndarray, M: 
     ref[m][k] = sum_n g[m][n] * w[n][k];  S[m][k] = sum_n |g[m][n] * w[n][k]|.
     """
     if cols is None:
-        w = dequant(scales, code_bytes, N, K).astype(np.float64)
+        w = dequant(scales, code_bytes, N, K)
     else:
-        w = dequant_columns(scales, code_bytes, N, K, cols).astype(np.float64)
-    g = np.asarray(grad_out, dtype=np.float32).reshape(M, N)
+        w = dequant_columns(scales, code_bytes, N, K, cols)
+    return grad_a_from_weights(grad_out, w, rows=rows, with_bound=with_bound)
+
+
+def grad_a_from_weights(grad_out: np.ndarray, w: np.ndarray, rows: np.ndarray | None = None,
+                        with_bound: bool = True):
+    """grad_a() with the fp32 weights already dequantised (w = dequant(...), [N][K'] for any column set).
+
+    ref[m][k] = sum_n g[m][n] * w[n][k] in fp64;  S[m][k] = sum_n |g[m][n] * w[n][k]|.
+    """
+    wd = np.asarray(w, dtype=np.float32).astype(np.float64)
+    N = wd.shape[0]
+    g = np.asarray(grad_out, dtype=np.float32).reshape(-1, N)
     if rows is not None:
         g = g[np.asarray(rows)]
     g = g.astype(np.float64)
-    ref = g @ w
+    ref = g @ wd
     if not with_bound:
         return ref
-    return ref, np.abs(g) @ np.abs(w)
+    return ref, np.abs(g) @ np.abs(wd)
 
 
 def forward(a: np.ndarray, scales: np.ndarray, code_bytes: np.ndarray, M: int, N: int, K: int,
@@ -181,8 +192,17 @@ def grad_a_fp16_operands(grad_out: np.ndarray, scales: np.ndarray, code_bytes: n
     it is not a gate, it exposes wrong operand rounding that the loose bound
     would hide.
     """
-    w16 = dequant(scales, code_bytes, N, K).astype(np.float16).astype(np.float64)
-    g = np.asarray(grad_out, dtype=np.float32).reshape(M, N)
+    return grad_a_fp16_operands_from_weights(grad_out, dequant(scales, code_bytes, N, K), rows=rows)
+
+
+def grad_a_fp16_operands_from_weights(grad_out: np.ndarray, w: np.ndarray, rows: np.ndarray | None = None):
+    """grad_a_fp16_operands() with the fp32 weights already dequantised (w = dequant(...), [N][K]).
+
+    Returns (sum_n fp16(g) * fp16(w), sum_n |fp16(g) * fp16(w)|), fp64, fp16() round-to-nearest-even.
+    """
+    w16 = np.asarray(w, dtype=np.float32).astype(np.float16).astype(np.float64)
+    N = w16.shape[0]
+    g = np.asarray(grad_out, dtype=np.float32).reshape(-1, N)
     if rows is not None:
         g = g[np.asarray(rows)]
     g16 = g.astype(np.float16).astype(np.float64)

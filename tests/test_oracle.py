@@ -308,6 +308,55 @@ def test_fp16_operand_reference_rounds_to_nearest_even():
         assert ref16[0, 0] == want
 
 
+# grad_out values (fp32) and their fp16 round-to-nearest-even images, worked out
+# by hand from the binary16 format (11 significant bits, normals down to 2^-14,
+# subnormals in steps of 2^-24, largest finite 65504): ties go to the even
+# significand, values below 2^-25 in magnitude round to zero.
+FP16_RNE_CASES = [
+    (1.0 + 2.0 ** -11, 1.0),                               # tie -> even (1.0)
+    (1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -9),               # tie -> even (1 + 2^-9)
+    (-(1.0 + 2.0 ** -11), -1.0),
+    (1.0 + 2.0 ** -11 + 2.0 ** -22, 1.0 + 2.0 ** -10),     # just above the tie -> up
+    (0.1, 1638.0 / 16384.0),                               # fp32 0.1 = 1638.4000... * 2^-14 -> 1638 * 2^-14
+    (2.0 ** -14 + 2.0 ** -25, 2.0 ** -14),                 # smallest normal: tie -> even
+    (2.0 ** -15 + 2.0 ** -25, 2.0 ** -15),                 # subnormal: 512.5 steps -> 512
+    (2.0 ** -15 + 3 * 2.0 ** -25, 514 * 2.0 ** -24),       # subnormal: 513.5 steps -> 514
+    (1.25 * 2.0 ** -24, 2.0 ** -24),                       # subnormal: 1.25 steps -> 1
+    (3 * 2.0 ** -25, 2 * 2.0 ** -24),                      # 1.5 steps -> 2 (even)
+    (2.0 ** -25, 0.0),                                     # 0.5 steps -> 0 (even)
+    (2.0 ** -26, 0.0),                                     # rounds to zero
+    (65504.0, 65504.0),                                    # largest finite
+    (65519.0, 65504.0),                                    # below the overflow midpoint 65520
+    (-65504.0, -65504.0),
+    (3.0, 3.0),
+]
+
+
+def test_fp16_operand_reference_rounds_grad_out_to_nearest_even():
+    """The diagnostic reference rounds grad_out to fp16 (RNE), checked against hand-worked values.
+
+    The weight is a single exact 1.0 (scale 1, code 15), so grad_A[m][0] is the
+    fp16 image of grad_out[m][0] itself and the bound scale is its magnitude.
+    Leaving grad_out in fp32, or rounding it any other way, fails here.
+    """
+    vals = np.array([v for v, _ in FP16_RNE_CASES], dtype=np.float32).reshape(-1, 1)
+    want = np.array([w for _, w in FP16_RNE_CASES], dtype=np.float64)
+    M = vals.shape[0]
+    b = np.full((1, 32), 0x77, dtype=np.uint8)
+    b[0, 0] = 0x7F                                         # code 15 (level 1.0) at k = 0, zeros elsewhere
+    s = np.ones((1, 1), dtype=np.float32)
+    ref16, S16 = oracle.grad_a_fp16_operands(vals, s, b, M, 1, 64)
+    assert np.array_equal(ref16[:, 0], want)
+    assert np.array_equal(S16[:, 0], np.abs(want))
+    assert np.all(ref16[:, 1:] == 0.0)
+    # the same values as one row against a column of unit weights: the sum of their fp16 images
+    # (every partial sum is exact in fp64)
+    b2 = np.full((M, 32), 0x77, dtype=np.uint8)
+    b2[:, 0] = 0x7F
+    ref16, _ = oracle.grad_a_fp16_operands(vals.reshape(1, M), np.ones((M, 1), dtype=np.float32), b2, 1, M, 64)
+    assert ref16[0, 0] == math.fsum(want)
+
+
 # ---------------------------------------------------------------------- pack
 
 def _pack_bruteforce(w_block):
