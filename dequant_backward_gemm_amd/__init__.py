@@ -26,7 +26,7 @@ import os
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libnf4bwd.so")
 
-NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_HIP = 0, 1, 2, 3, 4
+NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_HIP, NF4_ERR_CAPTURE = 0, 1, 2, 3, 4, 5
 
 EXPORTED_SYMBOLS = ("nf4_grad_a", "nf4_dequant", "nf4_pack", "nf4_status_string", "nf4_grad_a_plan",
                     "nf4_grad_a_forced", "nf4_release_workspaces", "nf4_forward", "nf4_forward_forced",
@@ -189,9 +189,8 @@ def grad_a_grouped(problems, outs=None, stream=None):
 
 
 def grad_a_forced(grad_out, scales, codes, kernel: str, rb: int = 2, splits: int = 1, out=None, stream=None):
-    """grad_a with a forced launch plan (kernel "tile", "skinny", "wide", "stream", "wide16", "unfused": the
-    comparison path with a separate fp16 dequant pass, or "wide16sk": wide16 tiles launched stream-K over
-    `splits` workgroups); for tests and tuning."""
+    """grad_a with a forced launch plan (kernel "tile", "skinny", "wide", "stream", "wide16", or "unfused": the
+    comparison path with a separate fp16 dequant pass); for tests and tuning."""
     import torch
     M, N = grad_out.shape
     K = codes.shape[1] * 2
@@ -201,7 +200,7 @@ def grad_a_forced(grad_out, scales, codes, kernel: str, rb: int = 2, splits: int
     if out is None:
         out = torch.empty((M, K), dtype=torch.float32, device=grad_out.device)
     _require(out, torch.float32, (M, K), "out")
-    kid = {"tile": 0, "skinny": 1, "wide": 3, "stream": 4, "wide16": 5, "unfused": 6, "wide16sk": 7}[kernel]
+    kid = {"tile": 0, "skinny": 1, "wide": 3, "stream": 4, "wide16": 5, "unfused": 6}[kernel]
     _check(_lib.nf4_grad_a_forced(_ptr(grad_out), _ptr(scales), _ptr(codes), _ptr(out), M, N, K, kid, rb, splits,
                                   _stream_handle(stream)), "nf4_grad_a_forced")
     return out
@@ -321,6 +320,5 @@ def grad_a_plan(M: int, N: int, K: int) -> dict:
     """Launch plan nf4_grad_a uses for a shape (host-only, no device work)."""
     out = (ctypes.c_int * 5)()
     _check(_lib.nf4_grad_a_plan(M, N, K, out), "nf4_grad_a_plan")
-    kernel = {0: "tile", 1: "skinny", 2: "zero_fill", 3: "wide", 4: "stream", 5: "wide16", 6: "unfused",
-              7: "wide16sk"}[out[0]]
+    kernel = {0: "tile", 1: "skinny", 2: "zero_fill", 3: "wide", 4: "stream", 5: "wide16", 6: "unfused"}[out[0]]
     return {"kernel": kernel, "rb": out[1], "splits": out[2], "n_chunk": out[3], "grid": out[4]}

@@ -17,7 +17,10 @@ bool dims_ok(int64_t a, int64_t b) {
   return a == 0 || b <= kMaxElems / a;
 }
 
-int from_hip(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_HIP; }
+int from_hip(hipError_t e) {
+  if (e == hipSuccess) return NF4_OK;
+  return e == hipErrorStreamCaptureUnsupported ? NF4_ERR_CAPTURE : NF4_ERR_HIP;
+}
 
 int forward_checked(const float* a, const float* scales, const uint8_t* codes, float* c, int64_t M, int64_t N,
                     int64_t K, int kernel, int splits, hipStream_t stream) {
@@ -182,6 +185,7 @@ const char* nf4_status_string(int status) {
     case NF4_ERR_SHAPE: return "bad shape (negative size, K not a multiple of 64, or size too large)";
     case NF4_ERR_ALIGN: return "pointer not 16-byte aligned";
     case NF4_ERR_HIP: return "HIP launch, allocation or synchronisation failed";
+    case NF4_ERR_CAPTURE: return "the stream's workspace would have to grow during HIP graph capture";
     default: return "unknown nf4 status";
   }
 }

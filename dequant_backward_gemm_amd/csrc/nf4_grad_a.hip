@@ -199,266 +199,6 @@ __global__ __launch_bounds__(256, (RB == 1 ? 2 : 1)) void grad_a_tile_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Tile kernel, fast path (N % 64 == 0): branch-free stage loop
-// ---------------------------------------------------------------------------
-// Same arithmetic and operand layouts as grad_a_tile_kernel, restructured so
-// that one 64-row stage of N is a single basic block the scheduler can
-// interleave:
-//  * every global load is in bounds by clamping instead of masking: rows of
-//    grad_out past M load row M-1, columns past K load the last column block,
-//    stages past the chunk reload its last stage.  Such values only reach
-//    outputs that are never stored (rows >= M, columns >= K) or LDS buffers
-//    that are never read, so no result changes;
-//  * codes and scales are prefetched two stages ahead, grad_out one stage
-//    ahead, and B fragments are read from LDS four MFMA slots ahead;
-//  * the NF4 levels sit at LDS address 0, so the lookup address of a code is
-//    4*code, one byte extract from a pre-shifted copy of the code word;
-//  * the decode of stage i+1 is spread between the MFMAs of stage i.
-constexpr int kLutBytes = 64;
-constexpr int kFragBytes = 2 * 4 * 8 * 64 * 16;
-
-// Fast path for full stages (N % 64 == 0): 4 waves, each owning 64 rows x
-// 256 columns of grad_A (two 32-row MFMA blocks x 8 tiles, 256 fp32
-// accumulators per lane), so a workgroup covers 256 x 256.  This wave tile is
-// the smallest that keeps both shared operands off the critical path: each
-// 1 KiB B fragment read from LDS feeds two 32x32x16 MFMAs, and each grad_out
-// byte loaded into registers feeds 256 columns.
-//
-// A stage (64 rows of N) is issued as 64 "ticks", one MFMA each, in a fixed
-// order enforced with scheduling barriers:
-//   * B fragments come from LDS through a ring of 4 registers;
-//   * grad_out rows of the next stage are loaded at ticks 0..15 and converted
-//     into the other A-fragment set at ticks 48..63 (the loop is unrolled twice
-//     so the two A sets swap names instead of being copied);
-//   * the next stage's codes are decoded column by column from tick 8 on:
-//     code words and scales come from a small per-wave LDS staging area, so no
-//     global load result is carried across a loop iteration in registers;
-//   * the codes of the stage after next are loaded at ticks 16..18 and stored
-//     to the staging area at the last tick.
-// The decode of a lane is the same as in grad_a_tile_kernel (8 rows x 8
-// columns, LDS level lookups, one fp32 multiply, packed fp16 pairs of rows).
-constexpr int kStageBytes = 16 * 32 * 4 + 16 * 4 * 4;  // per wave: 16 rows x 32 code words + 16 x 4 scales
-constexpr int kFastLds = kLutBytes + kFragBytes + 4 * kStageBytes;
-
-__global__ __launch_bounds__(256, 1) void grad_a_tile_fast_kernel(
-    const float* __restrict__ G, const float* __restrict__ S, const uint32_t* __restrict__ C32,
-    float* __restrict__ out, int M, int N, int K, int n_chunk, int tiles_m, int tiles_k) {
-  constexpr int RB = 2;        // 32-row blocks per wave
-  constexpr int BM = 256;
-  constexpr int T = 64;        // ticks (MFMAs) per stage
-  __shared__ __attribute__((aligned(16))) uint32_t smem[kFastLds / 4];
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int j = lane & 31, h = lane >> 5;
-
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int kt = logical % tiles_k;
-  const int rest = logical / tiles_k;
-  const int mt = rest % tiles_m;
-  const int split = rest / tiles_m;
-  const int m0 = mt * BM, k0 = kt * 256;
-  const int nb = split * n_chunk;
-  const int ne = min(N, nb + n_chunk);
-  const int nst = (ne - nb) >> 6;
-
-  if (tid < 16) lds_store_u32(smem, 4 * tid, __builtin_bit_cast(uint32_t, kLevels[tid]));
-
-  const __amdgpu_buffer_rsrc_t rc = make_rsrc(C32, (uint32_t)((size_t)N * (size_t)K / 2));
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, (uint32_t)((size_t)N * (size_t)(K / 64) * 4));
-  const __amdgpu_buffer_rsrc_t rg = make_rsrc(G, (uint32_t)((size_t)M * (size_t)N * 4));
-  const uint32_t crow = (uint32_t)K / 2;   // bytes per code row
-  const uint32_t srow = (uint32_t)K / 16;  // bytes per scale row
-  uint32_t voff_g[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = min(m0 + wave * 32 * RB + 32 * rb + j, M - 1);
-    voff_g[rb] = ((uint32_t)row * (uint32_t)N + 32u * h) * 4u;
-  }
-  // Staging loads: the wave's 16 decode rows are n0 + 32*(r/8) + 8*wave + r%8,
-  // r = 0..15.  Code load l (0, 1) of a lane covers row r = 8l + lane/8,
-  // 16 bytes at column chunk lane%8 (columns k0 + 32*(lane%8) ..), clamped
-  // into the array for a column tail; scale load: row lane/4, block lane%4.
-  const int sr_row = lane >> 3, sr_chunk = lane & 7;
-  const uint32_t voff_sc = (uint32_t)min(k0 / 2 + 16 * sr_chunk, K / 2 - 16) + (uint32_t)(8 * wave + sr_row) * crow;
-  const uint32_t voff_ss = (uint32_t)min(k0 / 64 + (lane & 3), K / 64 - 1) * 4u +
-                           (uint32_t)(32 * ((lane >> 2) >> 3) + 8 * wave + ((lane >> 2) & 7)) * srow;
-  const uint32_t stage_base = kLutBytes + kFragBytes + wave * kStageBytes;
-  const uint32_t frag_lane = kLutBytes + 16 * lane;
-
-  floatx16 acc[RB][8];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[rb][t][r] = 0.f;
-
-  auto stage_row = [&](int stage) { return (uint32_t)(nb + 64 * min(stage, nst - 1)); };
-  // code words (2 x 16 B) and one scale of stage `stage` into registers
-  auto load_stage_codes = [&](int stage, u32x4 (&cw)[2], uint32_t& sw) {
-    const uint32_t r0 = stage_row(stage);
-    cw[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, voff_sc, r0 * crow, 0));
-    cw[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, voff_sc, (r0 + 32) * crow, 0));
-    sw = __builtin_amdgcn_raw_buffer_load_b32(rs, voff_ss, r0 * srow, 0);
-  };
-  auto store_stage_codes = [&](const u32x4 (&cw)[2], uint32_t sw) {
-    lds_store_u32x4(smem, stage_base + (uint32_t)((sr_row * 32 + sr_chunk * 4) * 4), cw[0]);
-    lds_store_u32x4(smem, stage_base + (uint32_t)(((8 + sr_row) * 32 + sr_chunk * 4) * 4), cw[1]);
-    lds_store_u32(smem, stage_base + 16 * 32 * 4 + 4 * lane, sw);
-  };
-  // decode operands of the lane: code word of row (h, e) at column 8j, and its scale
-  auto read_code = [&](int e) { return lds_load_u32(smem, stage_base + (uint32_t)(((8 * h + e) * 32 + j) * 4)); };
-  auto read_scale = [&](int e) {
-    return lds_load_f32(smem, stage_base + 16 * 32 * 4 + (uint32_t)(((8 * h + e) * 4 + (j >> 3)) * 4));
-  };
-  // LDS byte address of the level of column t (0..7) of code word x is 4*code
-  auto lookup_x = [&](uint32_t x, int t) {
-    const uint32_t a = (t == 0) ? (x << 2) : (x >> (4 * t - 2));
-    return lds_load_f32(smem, a & 0x3Cu);
-  };
-  auto load_g1 = [&](int stage, int l, float (&an)[RB][32]) {  // l = 0..15: rb = l/8, 16-byte piece l%8
-    const int rb = l >> 3, v = l & 7;
-    const floatx4 q = __builtin_bit_cast(
-        floatx4, __builtin_amdgcn_raw_buffer_load_b128(rg, voff_g[rb] + 16u * v, stage_row(stage) * 4u, 0));
-    an[rb][4 * v + 0] = q[0];
-    an[rb][4 * v + 1] = q[1];
-    an[rb][4 * v + 2] = q[2];
-    an[rb][4 * v + 3] = q[3];
-  };
-
-  // Decode timeline: column t's 8 lookups at ticks 8+6t .. 8+6t+3 (two per
-  // tick), its scale/convert/store at ticks 8+6t+5 .. 8+6t+8.
-  constexpr int D0 = 8, P = 6;
-  static_assert(D0 + 7 * P + 8 < T, "decode must finish inside the stage");
-
-  auto stage = [&](int st, int cur, const u32x4 (&afc)[RB][4], u32x4 (&afn)[RB][4]) {
-    const uint32_t rbase = frag_lane + (uint32_t)(cur * 32768);
-    const uint32_t wbase = frag_lane + (uint32_t)(((cur ^ 1) * 4 + wave) * 8 * 1024);
-    // 8 registers for 4 slots of read-ahead: a reload never targets a register
-    // that an MFMA still in flight is reading
-    u32x4 ring[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ring[i] = lds_load_u32x4(smem, rbase + (uint32_t)(i * 1024));
-    uint32_t xd[8];
-    float sd[8];
-    float lk[2][8];
-    float an[RB][32];
-    u32x4 fv;
-    u32x4 cw[2];
-    uint32_t sw;
-    __builtin_amdgcn_sched_barrier(0);
-    auto tick = [&](auto kc) {
-      constexpr int k = decltype(kc)::value;
-      constexpr int i = k / RB, rb = k % RB;  // slot i = (k-step i/8, tile i%8)
-      if constexpr (k < 16) load_g1(st + 1, k, an);
-      if constexpr (k == 16) load_stage_codes(st + 2, cw, sw);
-      if constexpr (k < 8) {
-        xd[k] = read_code(k);
-        sd[k] = read_scale(k);
-      }
-      acc[rb][i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(afc[rb][i >> 3]), as_half8(ring[i & 7]),
-                                                              acc[rb][i & 7], 0, 0, 0);
-      if constexpr (rb == RB - 1 && i + 4 < 32)
-        ring[(i + 4) & 7] = lds_load_u32x4(smem, rbase + (uint32_t)((i + 4) * 1024));
-      if constexpr (k >= D0 && (k - D0) / P < 8 && (k - D0) % P < 4) {
-        constexpr int t = (k - D0) / P, m = (k - D0) % P;
-        lk[t & 1][2 * m] = lookup_x(xd[2 * m], t);
-        lk[t & 1][2 * m + 1] = lookup_x(xd[2 * m + 1], t);
-      }
-      if constexpr (k >= D0 + 5 && (k - D0 - 5) / P < 8 && (k - D0 - 5) % P < 4) {
-        constexpr int t = (k - D0 - 5) / P, m = (k - D0 - 5) % P;
-        fv[m] = pack_half2_rne(sd[2 * m] * lk[t & 1][2 * m], sd[2 * m + 1] * lk[t & 1][2 * m + 1]);
-        if constexpr (m == 3) lds_store_u32x4(smem, wbase + (uint32_t)(t * 1024), fv);
-      }
-      if constexpr (k >= 48) {
-        constexpr int c = 2 * (k - 48);  // two conversions per tick, 32 in all
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          constexpr int dummy = 0;
-          (void)dummy;
-          const int cc = c + u;
-          const int r2 = cc >> 4, s2 = (cc >> 2) & 3, p2 = cc & 3;
-          afn[r2][s2][p2] = pack_half2_rne(an[r2][8 * s2 + 2 * p2], an[r2][8 * s2 + 2 * p2 + 1]);
-        }
-      }
-      if constexpr (k == T - 1) store_stage_codes(cw, sw);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    for_each_index(std::make_integer_sequence<int, T>{}, tick);
-    __syncthreads();
-  };
-
-  u32x4 af0[RB][4], af1[RB][4];
-
-  // Prologue: stage 0 decoded straight from global memory into buffer 0,
-  // stage 1's codes staged in LDS, stage 0's A fragments in af0.
-  {
-    float an[RB][32];
-#pragma unroll
-    for (int l = 0; l < 16; ++l) load_g1(0, l, an);
-    u32x4 cw[2];
-    uint32_t sw;
-    load_stage_codes(0, cw, sw);
-    __syncthreads();  // levels visible
-    store_stage_codes(cw, sw);
-    uint32_t x0[8];
-    float s0[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      x0[e] = read_code(e);
-      s0[e] = read_scale(e);
-    }
-    load_stage_codes(1, cw, sw);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      float lk[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) lk[e] = lookup_x(x0[e], t);
-      u32x4 v;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) v[m] = pack_half2_rne(s0[2 * m] * lk[2 * m], s0[2 * m + 1] * lk[2 * m + 1]);
-      lds_store_u32x4(smem, frag_lane + (uint32_t)(wave * 8 * 1024 + t * 1024), v);
-    }
-    store_stage_codes(cw, sw);  // same wave reads it back in stage 0: program order suffices
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2)
-#pragma unroll
-        for (int p2 = 0; p2 < 4; ++p2) af0[rb][s2][p2] = pack_half2_rne(an[rb][8 * s2 + 2 * p2], an[rb][8 * s2 + 2 * p2 + 1]);
-    __syncthreads();
-  }
-
-  int st = 0;
-  for (; st + 1 < nst; st += 2) {
-    stage(st, 0, af0, af1);
-    stage(st + 1, 1, af1, af0);
-  }
-  if (st < nst) stage(st, 0, af0, af1);
-
-  float* __restrict__ dst = out + (size_t)split * (size_t)M * (size_t)K;
-  const int kk = k0 + 8 * j;
-  if (kk < K) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wave * 32 * RB + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < M) {
-          floatx4 lo = {acc[rb][0][r], acc[rb][1][r], acc[rb][2][r], acc[rb][3][r]};
-          floatx4 hi = {acc[rb][4][r], acc[rb][5][r], acc[rb][6][r], acc[rb][7][r]};
-          floatx4* o = reinterpret_cast<floatx4*>(dst + (size_t)row * (size_t)K + kk);
-          o[0] = lo;
-          o[1] = hi;
-        }
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Skinny kernel (1 <= M <= 16)
 // ---------------------------------------------------------------------------
 // 16x16x32 MFMA: A lane (i = lane%16, q = lane/16) holds A[i][8q..8q+7],
@@ -633,11 +373,10 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(floatx4* __restrict__ ou
 // ---------------------------------------------------------------------------
 // Launchers (called by the planner in nf4_plan.hip)
 // ---------------------------------------------------------------------------
-hipError_t launch_grad_a_tile(int rb, bool fast, int grid, const float* grad_out, const float* scales,
-                              const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,
-                              int tiles_k, hipStream_t stream) {
-  // the fast kernel has a fixed 256-row tile
-  auto kern = (fast && rb == 2) ? grad_a_tile_fast_kernel : (rb == 2 ? grad_a_tile_kernel<2> : grad_a_tile_kernel<1>);
+hipError_t launch_grad_a_tile(int rb, int grid, const float* grad_out, const float* scales, const uint32_t* codes,
+                              float* dst, int M, int N, int K, int n_chunk, int tiles_m, int tiles_k,
+                              hipStream_t stream) {
+  auto kern = rb == 2 ? grad_a_tile_kernel<2> : grad_a_tile_kernel<1>;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, grad_out, scales, codes, dst, M, N, K, n_chunk, tiles_m,
                      tiles_k);
   return hipGetLastError();

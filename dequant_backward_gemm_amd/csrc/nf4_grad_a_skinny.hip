@@ -23,9 +23,10 @@
 //   row per lane) through a 1 KiB per-wave LDS slot.
 //
 // N tails and chunk ends: rows n >= chunk end get scale 0 (so every table
-// entry, hence every decoded weight, is +-0) and grad_out 0; code rows past
-// the array read zero through the buffer range check.  Columns past K only
-// reach outputs that are not stored.
+// entry, hence every decoded weight, is +-0) and grad_out 0.  The scalar
+// (row) part of a code load's offset is clamped to the last row, so it stays
+// inside the array; the per-lane part beyond it reads zero through the
+// buffer range check.  Columns past K only reach outputs that are not stored.
 #include "nf4_kernel_util.h"
 #include "nf4_launch.h"
 
@@ -102,7 +103,8 @@ __device__ __forceinline__ void stream_strip(const float* __restrict__ G, const 
   auto load_step = [&](int j, Step& d) {
     const uint32_t n0 = (uint32_t)(nb + 32 * min(j, nsteps - 1));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) d.x[e] = __builtin_amdgcn_raw_buffer_load_b32(rc, cvoff, (n0 + e) * crow, 0);
+    for (int e = 0; e < 8; ++e)
+      d.x[e] = __builtin_amdgcn_raw_buffer_load_b32(rc, cvoff, min(n0 + e, (uint32_t)N - 1u) * crow, 0);
     d.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, svoff, n0 * srow, 0));
     if constexpr (VEC_A) {
 #pragma unroll

@@ -561,87 +561,6 @@ __global__ __launch_bounds__(512, 1) void grad_a_wide_kernel(
                            out + (size_t)split * (size_t)M * (size_t)K, K, 0, 0);
 }
 
-// Stream-K launch of the fragment-fed kernel.  The (tile, stage) iterations of
-// the whole product, tiles in (k-tile fastest, then m-tile) order and stages in
-// reduction order, are cut into `gridDim.x` equal contiguous ranges, one per
-// workgroup, so every CU gets the same amount of work whatever the tile count.
-// A workgroup walks its range tile by tile: a tile it covers whole is written
-// to grad_A directly; a piece of a tile split between workgroups (only a
-// range's first and last piece can be one) goes to the workgroup's partial
-// slot 2w (first piece) or 2w + 1 (last piece), BM x BK fp32, and
-// streamk_fixup_kernel adds a split tile's pieces in workgroup order, which is
-// reduction order.
-__device__ __forceinline__ int64_t streamk_begin(int w, int G, int64_t total) { return (int64_t)w * total / G; }
-
-__global__ __launch_bounds__(512, 1) void grad_a_wide_streamk_kernel(const void* __restrict__ frags,
-                                                                     const float* __restrict__ S,
-                                                                     const uint32_t* __restrict__ C32,
-                                                                     float* __restrict__ out,
-                                                                     float* __restrict__ slots, int M, int N, int K,
-                                                                     int tiles_m, int tiles_k) {
-  using Cfg = WideCfg<1>;
-  const int G = gridDim.x;
-  const int w = xcd_remap(blockIdx.x, G);
-  const int spt = N / 64;  // stages per tile
-  const int64_t total = (int64_t)tiles_m * tiles_k * spt;
-  const int64_t it1 = streamk_begin(w + 1, G, total);
-  int64_t it = streamk_begin(w, G, total);
-  const int64_t it0 = it;
-  while (it < it1) {
-    const int tile = (int)(it / spt);
-    const int st0 = (int)(it % spt);
-    const int st1 = (int)std::min<int64_t>((int64_t)spt, (int64_t)st0 + (it1 - it));
-    const bool whole = st0 == 0 && st1 == spt;
-    float* dst = whole ? out : slots + (size_t)(2 * w + (it == it0 ? 0 : 1)) * (size_t)(Cfg::BM * Cfg::BK);
-    wide_tile<1, WIDE_FRAG_DEPTH, false>(frags, S, C32, M, N, K, tiles_k, tile, 64 * st0, 64 * st1, dst,
-                                         whole ? K : Cfg::BK, whole ? 0 : (tile / tiles_k) * Cfg::BM,
-                                         whole ? 0 : (tile % tiles_k) * Cfg::BK);
-    it += st1 - st0;
-    __syncthreads();  // the next piece's prologue rewrites the LDS buffers
-  }
-}
-
-// Sums the pieces of every split tile (one workgroup per tile; tiles covered
-// by a single workgroup return at once): workgroups w_a .. w_b with a
-// non-empty share hold the tile's pieces in reduction order, each in slot 2w
-// if the piece starts its share, else 2w + 1.
-__global__ __launch_bounds__(512) void streamk_fixup_kernel(const float* __restrict__ slots, float* __restrict__ out,
-                                                            int M, int N, int K, int tiles_k, int G) {
-  using Cfg = WideCfg<1>;
-  const int tile = blockIdx.x;
-  const int spt = N / 64;
-  const int64_t total = (int64_t)gridDim.x * spt;
-  const int64_t t0 = (int64_t)tile * spt, t1 = t0 + spt;
-  // workgroup holding iteration i: the largest w with streamk_begin(w) <= i
-  auto owner = [&](int64_t i) {
-    int w = (int)((i * G) / total);
-    while (w + 1 < G && streamk_begin(w + 1, G, total) <= i) ++w;
-    while (w > 0 && streamk_begin(w, G, total) > i) --w;
-    return w;
-  };
-  const int wa = owner(t0), wb = owner(t1 - 1);
-  if (wa == wb) return;
-  const int m0 = (tile / tiles_k) * Cfg::BM, k0 = (tile % tiles_k) * Cfg::BK;
-  constexpr int kVec = Cfg::BM * Cfg::BK / 4;  // float4 elements per slot
-  for (int e = threadIdx.x; e < kVec; e += 512) {
-    floatx4 sum = {0.f, 0.f, 0.f, 0.f};
-    bool first = true;
-    for (int w = wa; w <= wb; ++w) {
-      const int64_t b = streamk_begin(w, G, total);
-      if (streamk_begin(w + 1, G, total) == b) continue;  // an empty share (more shares than iterations)
-      const int slot = 2 * w + (b >= t0 ? 0 : 1);
-      const floatx4 v = reinterpret_cast<const floatx4*>(slots + (size_t)slot * (size_t)(Cfg::BM * Cfg::BK))[e];
-      if (first)
-        sum = v;
-      else
-        sum += v;
-      first = false;
-    }
-    const int row = m0 + (4 * e) / Cfg::BK, col = k0 + (4 * e) % Cfg::BK;
-    if (row < M && col < K) *reinterpret_cast<floatx4*>(out + (size_t)row * (size_t)K + col) = sum;
-  }
-}
-
 // Grouped launch: the tiles of up to kWideGroupMax problems sharing M (each
 // fed by its fp16 A fragments, no N split) in one grid.  The host orders the
 // problems longest reduction first.  Tiles are dealt to the 8 XCDs in groups
@@ -680,18 +599,13 @@ bool wide_kernel_supported(int64_t M, int64_t N, int64_t K) {
          (uint64_t)N * (uint64_t)K / 2 < (1ull << 31);
 }
 
-int wide_tile_rows(int wc) { return wc == 2 ? WideCfg<2>::BM : WideCfg<1>::BM; }
-int wide_tile_cols(int wc) { return wc == 2 ? WideCfg<2>::BK : WideCfg<1>::BK; }
+int wide_tile_rows() { return WideCfg<1>::BM; }
+int wide_tile_cols() { return WideCfg<1>::BK; }
 
-hipError_t launch_grad_a_wide(int wc, int grid, const float* grad_out, const float* scales, const uint32_t* codes,
-                              float* dst, int M, int N, int K, int n_chunk, int tiles_m, int tiles_k,
-                              hipStream_t stream) {
-  if (wc == 2)
-    hipLaunchKernelGGL((grad_a_wide_kernel<2, 0>), dim3(grid), dim3(512), 0, stream, grad_out, scales, codes, dst, M,
-                       N, K, n_chunk, tiles_m, tiles_k);
-  else
-    hipLaunchKernelGGL((grad_a_wide_kernel<1, 0>), dim3(grid), dim3(512), 0, stream, grad_out, scales, codes, dst, M,
-                       N, K, n_chunk, tiles_m, tiles_k);
+hipError_t launch_grad_a_wide(int grid, const float* grad_out, const float* scales, const uint32_t* codes, float* dst,
+                              int M, int N, int K, int n_chunk, int tiles_m, int tiles_k, hipStream_t stream) {
+  hipLaunchKernelGGL((grad_a_wide_kernel<1, 0>), dim3(grid), dim3(512), 0, stream, grad_out, scales, codes, dst, M, N,
+                     K, n_chunk, tiles_m, tiles_k);
   return hipGetLastError();
 }
 
@@ -729,22 +643,6 @@ hipError_t launch_frag_pass(const float* src, void* frags, int rows, int cols, b
   else
     hipLaunchKernelGGL(grad_out_frag_kernel<false>, dim3(pgrid), dim3(256), 0, stream, src, static_cast<u32x4*>(frags),
                        rows, cols, total);
-  return hipGetLastError();
-}
-
-size_t streamk_slot_bytes(int grid) { return (size_t)grid * 2 * WideCfg<1>::BM * WideCfg<1>::BK * sizeof(float); }
-
-hipError_t launch_grad_a_wide_streamk(int grid, const float* grad_out, void* frags, float* slots, const float* scales,
-                                      const uint32_t* codes, float* out, int M, int N, int K, hipStream_t stream) {
-  hipError_t e = launch_frag_pass(grad_out, frags, M, N, /*natural=*/false, stream);
-  if (e != hipSuccess) return e;
-  const int tiles_m = (M + WideCfg<1>::BM - 1) / WideCfg<1>::BM, tiles_k = (K + WideCfg<1>::BK - 1) / WideCfg<1>::BK;
-  hipLaunchKernelGGL(grad_a_wide_streamk_kernel, dim3(grid), dim3(512), 0, stream, frags, scales, codes, out, slots, M,
-                     N, K, tiles_m, tiles_k);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(streamk_fixup_kernel, dim3(tiles_m * tiles_k), dim3(512), 0, stream, slots, out, M, N, K, tiles_k,
-                     grid);
   return hipGetLastError();
 }
 

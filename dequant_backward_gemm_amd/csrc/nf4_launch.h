@@ -22,14 +22,14 @@ hipError_t launch_grad_a(const float* grad_out, const float* scales, const uint8
 // Launch plan chosen for a shape (exposed for tests and the benchmark).
 struct GradAPlan {
   int kernel;    // 0 = tile (BM = 128 * rb), 1 = skinny (M <= 16), 2 = zero-fill (N == 0),
-                 // 3 = wide (8 waves, tile (512 / rb) x (128 * rb)), 4 = stream (M <= 16),
+                 // 3 = wide (8 waves, tile 512 x 128, fp32 grad_out converted in the loop),
+                 // 4 = stream (M <= 16),
                  // 5 = wide fed by fp16 A fragments from a conversion pass (tile 512 x 128),
-                 // 6 = unfused comparison path (fp16 weight pass, then a fragment-copy GEMM),
-                 // 7 = kernel 5's tiles launched stream-K (equal shares of all tile stages)
-  int rb;        // tile: 32-row blocks per wave; wide: 128-column groups
+                 // 6 = unfused comparison path (fp16 weight pass, then a fragment-copy GEMM)
+  int rb;        // tile: 32-row blocks per wave; wide: 1
   int splits;    // number of N-chunks (1 = no workspace, no reduce launch)
   int n_chunk;   // rows of N per chunk
-  int grid;      // workgroups of the main kernel (kernel 7: the number of shares)
+  int grid;      // workgroups of the main kernel
 };
 GradAPlan plan_grad_a(int64_t M, int64_t N, int64_t K);
 
@@ -47,30 +47,22 @@ constexpr int kWsCounters = 4096;
 hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** out, uint32_t** counters = nullptr);
 hipError_t release_workspaces();
 
-// Launch a given plan.
+// Launch a given plan (its partials and fragments in the stream's workspace).
 hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const float* scales, const uint8_t* codes,
                               float* grad_a, int64_t M, int64_t N, int64_t K, hipStream_t stream);
-
 // Wide tile kernel (nf4_grad_a_wide.hip): usable when N % 64 == 0 and the
-// operands have 32-bit byte offsets; tile shape for a column-group count.
+// operands have 32-bit byte offsets; its tile is wide_tile_rows() x
+// wide_tile_cols() (512 x 128).
 bool wide_kernel_supported(int64_t M, int64_t N, int64_t K);
-int wide_tile_rows(int wc);
-int wide_tile_cols(int wc);
-hipError_t launch_grad_a_wide(int wc, int grid, const float* grad_out, const float* scales, const uint32_t* codes,
-                              float* dst, int M, int N, int K, int n_chunk, int tiles_m, int tiles_k,
-                              hipStream_t stream);
+int wide_tile_rows();
+int wide_tile_cols();
+hipError_t launch_grad_a_wide(int grid, const float* grad_out, const float* scales, const uint32_t* codes, float* dst,
+                              int M, int N, int K, int n_chunk, int tiles_m, int tiles_k, hipStream_t stream);
 
 // Fragment-fed wide kernel: grad_out converted once to fp16 A fragments in a
 // workspace of wide_frag_bytes(M, N) bytes, then the wide kernel (tile 512 x
 // 128) reads them.  Same preconditions as the wide kernel.
 size_t wide_frag_bytes(int64_t M, int64_t N);
-// Stream-K launch of the fragment-fed wide kernel (kernel 7): `grid`
-// workgroups share the product's (tile, stage) iterations equally; pieces of
-// tiles split between workgroups go through streamk_slot_bytes(grid) bytes of
-// partial slots and a fixup kernel that adds them in reduction order.
-size_t streamk_slot_bytes(int grid);
-hipError_t launch_grad_a_wide_streamk(int grid, const float* grad_out, void* frags, float* slots, const float* scales,
-                                      const uint32_t* codes, float* out, int M, int N, int K, hipStream_t stream);
 hipError_t launch_grad_a_wide_frag(int grid, const float* grad_out, void* frags, const float* scales,
                                    const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,
                                    int tiles_k, hipStream_t stream);
@@ -204,9 +196,9 @@ hipError_t launch_grad_a_stream(int grid, const float* grad_out, const float* sc
                                 int tiles_k, int splits, hipStream_t stream);
 
 // Kernel launchers of nf4_grad_a.hip (tile, skinny, split reduction, zero fill).
-hipError_t launch_grad_a_tile(int rb, bool fast, int grid, const float* grad_out, const float* scales,
-                              const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,
-                              int tiles_k, hipStream_t stream);
+hipError_t launch_grad_a_tile(int rb, int grid, const float* grad_out, const float* scales, const uint32_t* codes,
+                              float* dst, int M, int N, int K, int n_chunk, int tiles_m, int tiles_k,
+                              hipStream_t stream);
 hipError_t launch_grad_a_skinny(int grid, const float* grad_out, const float* scales, const uint32_t* codes,
                                 float* dst, int M, int N, int K, int n_chunk, int tiles_k, hipStream_t stream);
 hipError_t launch_grad_a_reduce(int grid, const float* ws, float* out, int64_t n4, int splits, hipStream_t stream);

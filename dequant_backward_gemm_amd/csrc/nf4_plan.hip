@@ -45,6 +45,13 @@ hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** out, uint32
     hand_out();
     return hipSuccess;
   }
+  // Growing allocates (and frees the old buffer) in stream order, which must
+  // not happen inside a HIP graph capture: a captured graph would own the new
+  // buffer and keep a pointer to the freed one.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess) return e;
+  if (cap != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
   if (w == nullptr) {
     g_ws.push_back(Workspace{dev, stream, nullptr, 0});
     w = &g_ws.back();
@@ -189,20 +196,14 @@ GradAPlan plan_grad_a(int64_t M, int64_t N, int64_t K) {
   };
   // measured on MI355X (fraction of the fp16 MFMA rate at M = 8192): tile
   // kernel with 128-row tiles (two workgroups per CU) ~0.24, 256-row tiles
-  // ~0.19; wide kernel 512 x 128 tiles ~0.28, 256 x 256 tiles ~0.11; wide
-  // kernel fed by fp16 A fragments ~0.40, plus its conversion pass (reads 4
-  // and writes 2 bytes per grad_out element, ~5.5 TB/s, and a launch)
+  // ~0.19; wide kernel 512 x 128 tiles ~0.28; wide kernel fed by fp16 A
+  // fragments ~0.40, plus its conversion pass (reads 4 and writes 2 bytes per
+  // grad_out element, ~5.5 TB/s, and a launch)
   consider(0, 2, 256, 256, 1, 0.19, 0.0);
   consider(0, 1, 128, 256, 2, 0.24, 0.0);
   if (wide_kernel_supported(M, N, K)) {
-    consider(3, 1, wide_tile_rows(1), wide_tile_cols(1), 1, 0.28, 0.0);
-    consider(3, 2, wide_tile_rows(2), wide_tile_cols(2), 1, 0.11, 0.0);
-    consider(5, 1, wide_tile_rows(1), wide_tile_cols(1), 1, 0.40, 6.0 * (double)M * (double)N / 5.5e12 + 2e-6);
-    // (Kernel 7, the same tiles launched stream-K, is not considered: despite
-    // the even load it measured 3-32% slower than the plans above on every
-    // large and mid-size shape -- most likely because, with the shares'
-    // starting stages scattered, the workgroups of an XCD no longer walk one
-    // m-tile's grad_out fragments in step and stop sharing them in L2.)
+    consider(3, 1, wide_tile_rows(), wide_tile_cols(), 1, 0.28, 0.0);
+    consider(5, 1, wide_tile_rows(), wide_tile_cols(), 1, 0.40, 6.0 * (double)M * (double)N / 5.5e12 + 2e-6);
   }
   return p;
 }
@@ -246,23 +247,15 @@ bool make_plan(int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, 
     p.rb = 1;
     p.n_chunk = (int)chunk;
     p.splits = (int)cdiv(N, chunk);
-    p.grid = (int)(cdiv(M, wide_tile_rows(1)) * cdiv(K, wide_tile_cols(1)) * p.splits);
-  } else if (kernel == 7) {
-    // `splits` is the number of stream-K shares (workgroups)
-    if (!wide_kernel_supported(M, N, K)) return false;
-    p.kernel = 7;
-    p.rb = 1;
-    p.splits = 1;
-    p.n_chunk = (int)N;
-    p.grid = splits;
+    p.grid = (int)(cdiv(M, wide_tile_rows()) * cdiv(K, wide_tile_cols()) * p.splits);
   } else if (kernel == 3) {
-    if ((rb != 1 && rb != 2) || !wide_kernel_supported(M, N, K)) return false;
+    if (!wide_kernel_supported(M, N, K)) return false;
     const int64_t chunk = cdiv(cdiv(N, splits), 64) * 64;
     p.kernel = 3;
-    p.rb = rb;
+    p.rb = 1;
     p.n_chunk = (int)chunk;
     p.splits = (int)cdiv(N, chunk);
-    p.grid = (int)(cdiv(M, wide_tile_rows(rb)) * cdiv(K, wide_tile_cols(rb)) * p.splits);
+    p.grid = (int)(cdiv(M, wide_tile_rows()) * cdiv(K, wide_tile_cols()) * p.splits);
   } else {
     return false;
   }
@@ -273,6 +266,24 @@ bool make_plan(int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, 
 hipError_t launch_grad_a(const float* grad_out, const float* scales, const uint8_t* codes, float* grad_a,
                          int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   return launch_grad_a_plan(plan_grad_a(M, N, K), grad_out, scales, codes, grad_a, M, N, K, stream);
+}
+
+// Workspace layout of a plan: split partials (when N is split), then the fp16
+// A fragments (fragment-fed wide kernel), then the fp16 B fragments (unfused
+// comparison path), each 256-byte aligned.
+struct PlanWorkspace {
+  size_t part, part_al, frag, frag_al, bfrag;
+  size_t total() const { return part_al + frag_al + bfrag; }
+};
+static PlanWorkspace plan_workspace(const GradAPlan& p, int64_t M, int64_t N, int64_t K) {
+  PlanWorkspace w{};
+  if (p.kernel == 2) return w;
+  w.part = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)K * sizeof(float) : 0;
+  w.part_al = (w.part + 255) & ~(size_t)255;
+  w.frag = (p.kernel == 5 || p.kernel == 6) ? wide_frag_bytes(M, N) : 0;
+  w.frag_al = (w.frag + 255) & ~(size_t)255;
+  w.bfrag = p.kernel == 6 ? unfused_bfrag_bytes(N, K) : 0;
+  return w;
 }
 
 hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const float* scales, const uint8_t* codes,
@@ -289,20 +300,15 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
   const bool fused_reduce = p.kernel == 4 && p.splits > 1 && cdiv(K, kStreamBK) <= kWsCounters &&
                             (uint64_t)p.splits * (uint64_t)M * (uint64_t)K * 4 < (1ull << 32);
   {
-    // workspace: split partials, then (fragment-fed wide kernel) the fp16 A fragments
-    const size_t part = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)K * sizeof(float) : 0;
-    const size_t part_al = (part + 255) & ~(size_t)255;
-    const size_t frag = (p.kernel == 5 || p.kernel == 6 || p.kernel == 7) ? wide_frag_bytes(M, N) : 0;
-    const size_t frag_al = (frag + 255) & ~(size_t)255;
-    const size_t bfrag = p.kernel == 6 ? unfused_bfrag_bytes(N, K) : p.kernel == 7 ? streamk_slot_bytes(p.grid) : 0;
-    if (part + frag + bfrag > 0) {
+    const PlanWorkspace w = plan_workspace(p, M, N, K);
+    if (w.total() > 0) {
       char* base = nullptr;
-      hipError_t e = stream_workspace(stream, part_al + frag_al + bfrag, reinterpret_cast<void**>(&base),
+      hipError_t e = stream_workspace(stream, w.total(), reinterpret_cast<void**>(&base),
                                       fused_reduce ? &counters : nullptr);
       if (e != hipSuccess) return e;
-      if (part) ws = reinterpret_cast<float*>(base);
-      if (frag) frags = base + part_al;
-      if (bfrag) bfrags = base + part_al + frag_al;
+      if (w.part) ws = reinterpret_cast<float*>(base);
+      if (w.frag) frags = base + w.part_al;
+      if (w.bfrag) bfrags = base + w.part_al + w.frag_al;
     }
     if (ws) dst = ws;
   }
@@ -315,21 +321,15 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
                              (int)cdiv(K, kStreamBK), p.splits, stream);
   } else if (p.kernel == 6) {
     e = launch_grad_a_unfused(p.grid, grad_out, frags, bfrags, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
-                              (int)cdiv(M, wide_tile_rows(1)), (int)cdiv(K, wide_tile_cols(1)), stream);
-  } else if (p.kernel == 7) {
-    e = launch_grad_a_wide_streamk(p.grid, grad_out, frags, static_cast<float*>(bfrags), scales, c32, dst, (int)M,
-                                   (int)N, (int)K, stream);
+                              (int)cdiv(M, wide_tile_rows()), (int)cdiv(K, wide_tile_cols()), stream);
   } else if (p.kernel == 5) {
     e = launch_grad_a_wide_frag(p.grid, grad_out, frags, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
-                                (int)cdiv(M, wide_tile_rows(1)), (int)cdiv(K, wide_tile_cols(1)), stream);
+                                (int)cdiv(M, wide_tile_rows()), (int)cdiv(K, wide_tile_cols()), stream);
   } else if (p.kernel == 3) {
-    e = launch_grad_a_wide(p.rb, p.grid, grad_out, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
-                           (int)cdiv(M, wide_tile_rows(p.rb)), (int)cdiv(K, wide_tile_cols(p.rb)), stream);
+    e = launch_grad_a_wide(p.grid, grad_out, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
+                           (int)cdiv(M, wide_tile_rows()), (int)cdiv(K, wide_tile_cols()), stream);
   } else {
-    // fast path: every stage of every chunk is full and every array has 32-bit byte offsets
-    const bool fast = (N % 64) == 0 && (uint64_t)M * (uint64_t)N * 4 < (1ull << 31) &&
-                      (uint64_t)N * (uint64_t)K / 2 < (1ull << 31);
-    e = launch_grad_a_tile(p.rb, fast, p.grid, grad_out, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
+    e = launch_grad_a_tile(p.rb, p.grid, grad_out, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
                            (int)cdiv(M, 128 * p.rb), tiles_k, stream);
   }
   if (e != hipSuccess) return e;
@@ -565,7 +565,7 @@ hipError_t launch_grad_a_grouped(const float* const* grad_out, const float* cons
   WideGroup g{};
   g.count = ng;
   g.M = (int)M;
-  g.tiles_m = (int)cdiv(M, wide_tile_rows(1));
+  g.tiles_m = (int)cdiv(M, wide_tile_rows());
   int begin = 0;
   for (int j = 0; j < ng; ++j) {
     const int i = idx[j];
@@ -578,7 +578,7 @@ hipError_t launch_grad_a_grouped(const float* const* grad_out, const float* cons
     w.out = grad_a[i];
     w.N = (int)N[i];
     w.K = (int)K[i];
-    w.tiles_k = (int)cdiv(K[i], wide_tile_cols(1));
+    w.tiles_k = (int)cdiv(K[i], wide_tile_cols());
     w.tile_begin = begin;
     begin += g.tiles_m * w.tiles_k;
   }

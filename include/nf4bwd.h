@@ -35,23 +35,33 @@
  *     nothing has been enqueued.  NF4_ERR_HIP reports a failed launch or a
  *     failed stream-ordered allocation (hipGetLastError); the stream's later
  *     work is then undefined.
- *   - State kept across calls: the workspace of nf4_grad_a / nf4_forward, one
- *     device buffer per (device, stream) that has needed one, grown on
- *     demand and held until nf4_release_workspaces().  Calls on one stream
- *     share it (they run in order); concurrent calls on different streams
- *     use different buffers and are safe.  Calls on one stream must be issued
- *     from one host thread at a time (a call that grows the buffer frees the
- *     old one in stream order, before work another thread enqueues later).
- *     A stream handle that is destroyed while its calls are still running
- *     must not be reused by a new stream before they finish (the new stream
- *     would inherit the buffer).  The buffer starts with per-strip arrival
- *     counters, zeroed when it is allocated; the streaming kernels count
- *     their split workgroups on them and leave them at zero.
+ *   - State kept across calls: the workspace of nf4_grad_a / nf4_forward /
+ *     nf4_rms_norm_backward, one device buffer per (device, stream) that has
+ *     needed one, grown on demand and held until nf4_release_workspaces().
+ *     (A stream-ordered allocate/free pair per call costs more host time than
+ *     a skinny call's kernels take, so the buffer is cached rather than
+ *     allocated per call.)  Calls on one stream share it (they run in order);
+ *     concurrent calls on different streams use different buffers and are
+ *     safe.  Calls on one stream must be issued from one host thread at a time
+ *     (a call that grows the buffer frees the old one in stream order, before
+ *     work another thread enqueues later).  A stream handle that is destroyed
+ *     while its calls are still running must not be reused by a new stream
+ *     before they finish (the new stream would inherit the buffer).  The
+ *     buffer starts with per-strip arrival counters, zeroed when it is
+ *     allocated; the streaming kernels count their split workgroups on them
+ *     and leave them at zero.
  *   - HIP graphs: the calls can be captured on a stream and replayed, as long
  *     as the stream's workspace already holds what they need (an eager call
- *     of the same shapes on that stream before capture); a capture that has
- *     to grow the workspace would allocate inside the graph.  No call issues
- *     hipMemset (buffers are cleared by kernels).
+ *     of the same shapes on that stream before capture).  A call that would
+ *     have to grow the workspace while its stream is capturing returns
+ *     NF4_ERR_CAPTURE and enqueues nothing.  A captured graph keeps the
+ *     address of the capture stream's workspace: growing that workspace later
+ *     (a larger call on the stream) or nf4_release_workspaces() frees it and
+ *     invalidates the graph.  A replay uses the capture stream's workspace
+ *     wherever it is launched, so it must not overlap other work that uses it
+ *     (eager calls on the capture stream, or another replay of a graph
+ *     captured there).  No call issues hipMemset (buffers are cleared by
+ *     kernels).
  */
 #ifndef NF4BWD_H
 #define NF4BWD_H
@@ -68,7 +78,8 @@ typedef enum nf4_status {
   NF4_ERR_NULL = 1,   /* a required pointer is NULL while its array is non-empty */
   NF4_ERR_SHAPE = 2,  /* negative size, K % 64 != 0, or a size over 2^31-1 */
   NF4_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned */
-  NF4_ERR_HIP = 4     /* a HIP launch, allocation or synchronisation failed */
+  NF4_ERR_HIP = 4,    /* a HIP launch, allocation or synchronisation failed */
+  NF4_ERR_CAPTURE = 5 /* the stream's workspace would have to grow during graph capture */
 } nf4_status;
 
 /*
@@ -118,13 +129,12 @@ const char* nf4_status_string(int status);
 /*
  * nf4_grad_a_plan -- host-only introspection of the launch plan nf4_grad_a
  * uses for a shape (no device work).  out5 receives, in order: kernel
- * (0 = tiled, 1 = skinny M <= 16, 2 = zero fill for N == 0, 3 = wide tiled,
- * 4 = streaming M <= 16 with 128-column strips, 5 = wide tiled fed by an fp16
- * A-fragment conversion pass of grad_out, 7 = kernel 5's tiles launched
- * stream-K), the kernel's tile parameter
- * (tiled: 32-row blocks per wave; wide: column groups of 128, the tile being
- * 512 x 128 or 256 x 256; 0 for the others), number of N-chunks
- * (1 = no split partials), rows per N-chunk, workgroups of the main launch.
+ * (0 = tiled, 1 = skinny M <= 16, 2 = zero fill for N == 0, 3 = wide tiled
+ * 512 x 128 converting fp32 grad_out in its loop, 4 = streaming M <= 16 with
+ * 128-column strips, 5 = wide tiled 512 x 128 fed by an fp16 A-fragment
+ * conversion pass of grad_out), the kernel's tile parameter (tiled: 32-row
+ * blocks per wave; wide: 1; 0 for the others), number of N-chunks (1 = no
+ * split partials), rows per N-chunk, workgroups of the main launch.
  * Returns NF4_ERR_SHAPE / NF4_ERR_NULL like nf4_grad_a.
  */
 int nf4_grad_a_plan(int64_t M, int64_t N, int64_t K, int* out5);
@@ -132,24 +142,19 @@ int nf4_grad_a_plan(int64_t M, int64_t N, int64_t K, int* out5);
 /*
  * nf4_grad_a_forced -- nf4_grad_a with the launch plan forced, for tests and
  * tuning: kernel 0 = tiled with `rb` (1 or 2) 32-row blocks per wave, kernel
- * 1 = skinny (requires M <= 16), kernel 3 = wide tiled with `rb` (1 or 2)
- * column groups (requires N % 64 == 0 and grad_out and the codes below 2 GiB),
- * kernel 4 = streaming (requires M <= 16 and grad_out and the codes below
- * 2 GiB; `rb` ignored), kernel 5 = wide tiled 512 x 128 fed by the fp16
- * A-fragment pass (same requirements as kernel 3; `rb` ignored; the fragments
- * take 2 * 16*ceil(M/16) * N bytes of the split-N workspace), kernel 6 = the
+ * 1 = skinny (requires M <= 16), kernel 3 = wide tiled 512 x 128 (requires
+ * N % 64 == 0 and grad_out and the codes below 2 GiB; `rb` ignored), kernel
+ * 4 = streaming (requires M <= 16 and grad_out and the codes below 2 GiB;
+ * `rb` ignored), kernel 5 = wide tiled 512 x 128 fed by the fp16 A-fragment
+ * pass (same requirements as kernel 3; `rb` ignored; the fragments take
+ * 2 * 16*ceil(M/16) * N bytes of the split-N workspace), kernel 6 = the
  * unfused comparison path: the weights dequantised to fp16 by a separate pass
  * (2 * N * 128*ceil(K/128) bytes of workspace), then the kernel-5 GEMM
  * reading them instead of decoding (same requirements, bitwise the same
- * result as kernel 5), kernel 7 = kernel 5's tiles launched stream-K: `splits`
- * workgroups each take an equal contiguous share of all (tile, 64-row stage)
- * iterations, a tile split between workgroups is summed from their fp32
- * pieces in reduction order by a fixup kernel (2 * splits * 512 * 128 * 4
- * bytes of workspace besides the fragments; `rb` ignored);
- * otherwise `splits` = requested number of N-chunks
- * (rounded so that every chunk but the last is a whole number of stages).
- * Same contract and results-to-bound as nf4_grad_a; NF4_ERR_SHAPE if the
- * forced plan does not fit the shape.
+ * result as kernel 5); `splits` = requested number of N-chunks (rounded so
+ * that every chunk but the last is a whole number of stages).  Same contract
+ * and results-to-bound as nf4_grad_a; NF4_ERR_SHAPE if the forced plan does
+ * not fit the shape.
  */
 int nf4_grad_a_forced(const float* grad_out, const float* scales, const uint8_t* codes, float* grad_a,
                       int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, hipStream_t stream);

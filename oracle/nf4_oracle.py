@@ -142,7 +142,8 @@ def grad_a(grad_out: np.ndarray, scales: np.ndarray, code_bytes: np.ndarray, M: 
         w = dequant(scales, code_bytes, N, K)
     else:
         w = dequant_columns(scales, code_bytes, N, K, cols)
-    return grad_a_from_weights(grad_out, w, rows=rows, with_bound=with_bound)
+    g = np.asarray(grad_out, dtype=np.float32).reshape(M, N)
+    return grad_a_from_weights(g, w, rows=rows, with_bound=with_bound)
 
 
 def grad_a_from_weights(grad_out: np.ndarray, w: np.ndarray, rows: np.ndarray | None = None,
@@ -152,8 +153,9 @@ def grad_a_from_weights(grad_out: np.ndarray, w: np.ndarray, rows: np.ndarray | 
     ref[m][k] = sum_n g[m][n] * w[n][k] in fp64;  S[m][k] = sum_n |g[m][n] * w[n][k]|.
     """
     wd = np.asarray(w, dtype=np.float32).astype(np.float64)
-    N = wd.shape[0]
-    g = np.asarray(grad_out, dtype=np.float32).reshape(-1, N)
+    g = np.asarray(grad_out, dtype=np.float32)
+    if g.ndim != 2 or g.shape[1] != wd.shape[0]:
+        raise ValueError(f"grad_out must be [M][N] with N = {wd.shape[0]}, got shape {g.shape}")
     if rows is not None:
         g = g[np.asarray(rows)]
     g = g.astype(np.float64)
@@ -192,7 +194,8 @@ def grad_a_fp16_operands(grad_out: np.ndarray, scales: np.ndarray, code_bytes: n
     it is not a gate, it exposes wrong operand rounding that the loose bound
     would hide.
     """
-    return grad_a_fp16_operands_from_weights(grad_out, dequant(scales, code_bytes, N, K), rows=rows)
+    g = np.asarray(grad_out, dtype=np.float32).reshape(M, N)
+    return grad_a_fp16_operands_from_weights(g, dequant(scales, code_bytes, N, K), rows=rows)
 
 
 def grad_a_fp16_operands_from_weights(grad_out: np.ndarray, w: np.ndarray, rows: np.ndarray | None = None):
@@ -201,8 +204,9 @@ def grad_a_fp16_operands_from_weights(grad_out: np.ndarray, w: np.ndarray, rows:
     Returns (sum_n fp16(g) * fp16(w), sum_n |fp16(g) * fp16(w)|), fp64, fp16() round-to-nearest-even.
     """
     w16 = np.asarray(w, dtype=np.float32).astype(np.float16).astype(np.float64)
-    N = w16.shape[0]
-    g = np.asarray(grad_out, dtype=np.float32).reshape(-1, N)
+    g = np.asarray(grad_out, dtype=np.float32)
+    if g.ndim != 2 or g.shape[1] != w16.shape[0]:
+        raise ValueError(f"grad_out must be [M][N] with N = {w16.shape[0]}, got shape {g.shape}")
     if rows is not None:
         g = g[np.asarray(rows)]
     g16 = g.astype(np.float16).astype(np.float64)

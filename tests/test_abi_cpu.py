@@ -43,8 +43,9 @@ def test_library_exports_every_declared_symbol(nb):
 
 
 def test_status_strings(nb):
-    for s in range(5):
-        assert nb.status_string(s)
+    for s in range(6):
+        assert nb.status_string(s) and "unknown" not in nb.status_string(s)
+    assert "capture" in nb.status_string(nb.NF4_ERR_CAPTURE)
     assert "unknown" in nb.status_string(99)
 
 
@@ -111,7 +112,6 @@ def test_plan_is_consistent(nb, M, N, K):
         bm = 128 * p["rb"]
         assert p["grid"] == -(-M // bm) * tiles_k * p["splits"]
     else:
-        assert p["n_chunk"] % 64 == 0 and p["rb"] in (1, 2)
-        assert p["kernel"] == "wide" or p["rb"] == 1
-        bm, bk = 512 // p["rb"], 128 * p["rb"]
+        assert p["n_chunk"] % 64 == 0 and p["rb"] == 1
+        bm, bk = 512, 128
         assert p["grid"] == -(-M // bm) * -(-K // bk) * p["splits"]

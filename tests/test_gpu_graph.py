@@ -66,3 +66,40 @@ def test_calls_in_a_graph_match_eager(lib):
         want = outs + [c_fwd] + grp_out + fgrp_out
         for k, (x, y) in enumerate(zip(got, want)):
             assert torch.equal(x.view(torch.int32), y.view(torch.int32)), (rep, k)
+
+
+def test_capture_that_would_grow_the_workspace_is_refused(lib):
+    """A call whose stream is capturing and whose workspace would have to grow returns NF4_ERR_CAPTURE and
+    enqueues nothing (the graph stays valid); once an eager call has sized the workspace, the same call can be
+    captured and its replay matches eager."""
+    lib.release_workspaces()  # every stream starts without a workspace
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        g, s, b = _inputs(16, 3000, 512, seed=900)
+        o = torch.empty((16, 512), device="cuda")
+        x = torch.zeros(4, device="cuda")
+    st.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    raised = None
+    with torch.cuda.graph(graph, stream=st):
+        try:
+            lib.grad_a_forced(g, s, b, "stream", rb=0, splits=4, out=o)
+        except lib.Nf4Error as e:
+            raised = e
+        x.add_(1.0)
+    assert raised is not None and raised.status == lib.NF4_ERR_CAPTURE, raised
+    graph.replay()
+    st.synchronize()
+    assert torch.equal(x, torch.ones(4, device="cuda"))
+    with torch.cuda.stream(st):
+        lib.grad_a_forced(g, s, b, "stream", rb=0, splits=4, out=o)  # eager: sizes the workspace
+    st.synchronize()
+    want = o.clone()
+    o.fill_(float("nan"))
+    torch.cuda.synchronize()
+    graph2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph2, stream=st):
+        lib.grad_a_forced(g, s, b, "stream", rb=0, splits=4, out=o)
+    graph2.replay()
+    st.synchronize()
+    assert torch.equal(o.view(torch.int32), want.view(torch.int32))

@@ -160,11 +160,12 @@ def test_grad_a_tile_variants_ragged(lib, kernel, rb, splits, M, N, K):
                  what=f"{kernel} rb{rb} s{splits} {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("rb,splits", [(1, 1), (2, 1), (1, 3), (2, 2)])
+@pytest.mark.parametrize("rb,splits", [(1, 1), (1, 2), (1, 3)])
 @pytest.mark.parametrize("M,N,K", [(17, 64, 64), (200, 384, 768), (513, 640, 320), (600, 1024, 448),
                                    (1030, 256, 1088)])
 def test_grad_a_wide_variants_ragged(lib, rb, splits, M, N, K):
-    """Wide tile kernel (N % 64 == 0): 512x128 and 256x256 tiles, ragged M and K tails, N splits."""
+    """Wide tile kernel (N % 64 == 0), fp32 grad_out converted in the loop: 512x128 tiles, ragged M and K
+    tails, N splits."""
     g, s, b = random_inputs(M, N, K, seed=M + 7 * N + K + rb * 13 + splits)
     check_grad_a(lib, g, s, b, M, N, K, kernel="wide", rb=rb, splits=splits,
                  what=f"wide rb{rb} s{splits} {M}x{N}x{K}")
@@ -193,36 +194,6 @@ def test_grad_a_wide16_matches_wide_bitwise(lib):
         assert np.array_equal(r1.view(np.uint32), r2.view(np.uint32))
     with pytest.raises(lib.Nf4Error):
         lib.grad_a_forced(dev(g[:, :2000]), sd[:2000], bd[:2000], "wide16", rb=1)
-
-
-@pytest.mark.parametrize("shares", [1, 3, 7, 64, 256])
-@pytest.mark.parametrize("M,N,K", [(17, 64, 64), (200, 384, 768), (513, 640, 320), (600, 1024, 448),
-                                   (1030, 256, 1088), (31, 128, 128)])
-def test_grad_a_streamk_ragged(lib, shares, M, N, K):
-    """Stream-K launch of the wide16 tiles: shares from 1 (one workgroup walks every tile) to more shares
-    than (tile, stage) iterations (empty shares), tiles split between two or more workgroups and summed
-    by the fixup, ragged M and K."""
-    g, s, b = random_inputs(M, N, K, seed=M + 3 * N + K + 11 * shares)
-    check_grad_a(lib, g, s, b, M, N, K, kernel="wide16sk", rb=1, splits=shares,
-                 what=f"wide16sk G{shares} {M}x{N}x{K}")
-
-
-def test_grad_a_streamk_unsplit_tiles_match_wide16_bitwise(lib):
-    """With one share, or shares that hold whole tiles only, no tile is split: every tile runs the wide16
-    body over its full reduction and the results equal the plain launch bit for bit; split tiles are
-    repeatable bit for bit."""
-    M, N, K = 600, 1024, 512  # 2 x 4 tiles of 16 stages
-    g, s, b = random_inputs(M, N, K, seed=41)
-    gd, sd, bd = dev(g), dev(s), dev(b)
-    base = host(lib.grad_a_forced(gd, sd, bd, "wide16", rb=1, splits=1))
-    for shares in (1, 2, 4, 8):
-        r = host(lib.grad_a_forced(gd, sd, bd, "wide16sk", rb=1, splits=shares))
-        assert np.array_equal(r.view(np.uint32), base.view(np.uint32)), shares
-    r1 = host(lib.grad_a_forced(gd, sd, bd, "wide16sk", rb=1, splits=5))
-    r2 = host(lib.grad_a_forced(gd, sd, bd, "wide16sk", rb=1, splits=5))
-    assert np.array_equal(r1.view(np.uint32), r2.view(np.uint32))
-    ref, S = oracle.grad_a(g, s, b, M, N, K)
-    assert_within_bound(r1, ref, S, "wide16sk G5")
 
 
 @pytest.mark.parametrize("splits", [1, 3])
@@ -316,7 +287,7 @@ def test_grad_a_wide_deterministic_and_rejects_ragged_n(lib):
     M, N, K = 700, 4096, 384
     g, s, b = random_inputs(M, N, K, seed=31)
     gd, sd, bd = dev(g), dev(s), dev(b)
-    for rb, splits in [(1, 1), (2, 3)]:
+    for rb, splits in [(1, 1), (1, 3)]:
         r1 = host(lib.grad_a_forced(gd, sd, bd, "wide", rb=rb, splits=splits))
         r2 = host(lib.grad_a_forced(gd, sd, bd, "wide", rb=rb, splits=splits))
         assert np.array_equal(r1.view(np.uint32), r2.view(np.uint32))
@@ -418,7 +389,7 @@ def test_grad_a_mlp_pair_config(lib, which, seed):
     M, N, K = shp.M, shp.N, shp.K
     s, b = packed_weights(N, K, seed=seed)
     g = synth.grad_out_normal(M, N, seed=seed + 100, std=1e-2)
-    check_grad_a(lib, g, s, b, M, N, K, what=shp.name, diag=False)
+    check_grad_a(lib, g, s, b, M, N, K, what=shp.name)
 
 
 @pytest.mark.parametrize("shp", synth.SKINNY_SHAPES, ids=lambda s: s.name)
@@ -428,22 +399,6 @@ def test_grad_a_skinny_config(lib, shp):
     s, b = packed_weights(N, K, seed=seed)
     g = synth.grad_out_normal(M, N, seed=10 + M, std=1.0)
     check_grad_a(lib, g, s, b, M, N, K, what=shp.name)
-
-
-@pytest.mark.parametrize("proj", ["q", "k", "gate", "down"])
-def test_grad_a_full_step_shapes_sampled_rows(lib, proj):
-    """Full-step projections at M = 8192 with the production plan; 16 rows checked."""
-    N, K = {p: (n, k) for (p, n, k) in synth.FULL_STEP_PROJECTIONS}[proj]
-    M = 8192
-    s, b = packed_weights(N, K, seed=100 + ["q", "k", "v", "o", "gate", "up", "down"].index(proj))
-    g = synth.grad_out_normal(M, N, seed=200, std=1e-2)
-    out = lib.grad_a(dev(g), dev(s), dev(b))
-    gpu = host(out)
-    assert np.all(np.isfinite(gpu))
-    rng = np.random.default_rng(300)
-    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, size=14)]))
-    ref, S = oracle.grad_a(g, s, b, M, N, K, rows=rows)
-    assert_within_bound(gpu[rows], ref, S, f"full_step {proj}")
 
 
 # ------------------------------------------------- maximum sizes: operands of 2 GiB and more

@@ -219,6 +219,13 @@ def test_grad_a_special_cases():
         onehot[:, 1::2] = hi == v
         alt += float(oracle.NF4_LEVELS[v]) * (g.astype(np.float64) @ onehot)
     assert np.allclose(ref, alt, rtol=1e-12, atol=1e-12)
+    # N = 0: the empty sum, zeros of shape M x K, in both the definition and the fp16-operand reference
+    g0 = np.zeros((M, 0), dtype=np.float32)
+    s0 = np.zeros((0, K // 64), dtype=np.float32)
+    b0 = np.zeros((0, K // 2), dtype=np.uint8)
+    for fn in (oracle.grad_a, oracle.grad_a_fp16_operands):
+        ref, S = fn(g0, s0, b0, M, 0, K)
+        assert ref.shape == (M, K) and np.all(ref == 0.0) and np.all(S == 0.0)
 
 
 # ----------------------------------------------------------------- forward C = A . W^T
