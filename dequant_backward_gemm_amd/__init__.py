@@ -26,11 +26,12 @@ import os
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libnf4bwd.so")
 
-NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_HIP, NF4_ERR_CAPTURE = 0, 1, 2, 3, 4, 5
+NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_HIP, NF4_ERR_CAPTURE, NF4_ERR_SCRATCH = 0, 1, 2, 3, 4, 5, 6
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 EXPORTED_SYMBOLS = ("nf4_grad_a", "nf4_dequant", "nf4_pack", "nf4_status_string", "nf4_grad_a_plan",
                     "nf4_grad_a_forced", "nf4_release_workspaces", "nf4_forward", "nf4_forward_forced",
-                    "nf4_grad_a_grouped", "nf4_rms_norm_backward", "nf4_forward_grouped")
+                    "nf4_grad_a_grouped", "nf4_rms_norm_backward", "nf4_forward_grouped", "nf4_grad_a_noalloc")
 GROUP_MAX = 8
 
 
@@ -67,6 +68,8 @@ def _load() -> ctypes.CDLL:
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.nf4_grad_a.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     lib.nf4_grad_a.restype = ctypes.c_int
+    lib.nf4_grad_a_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.nf4_grad_a_noalloc.restype = ctypes.c_int
     lib.nf4_dequant.argtypes = [vp, vp, vp, i64, i64, vp]
     lib.nf4_dequant.restype = ctypes.c_int
     lib.nf4_pack.argtypes = [vp, vp, vp, i64, i64, vp]
@@ -157,6 +160,22 @@ def grad_a(grad_out, scales, codes, out=None, stream=None):
     _require(out, torch.float32, (M, K), "out")
     _check(grad_a_raw(_ptr(grad_out), _ptr(scales), _ptr(codes), _ptr(out), M, N, K, _stream_handle(stream)),
            "nf4_grad_a")
+    return out
+
+
+def grad_a_noalloc(grad_out, scales, codes, out, stream=None):
+    """grad_a through nf4_grad_a_noalloc: no device allocation by the library (its scratch is a static
+    device array); `out` must be given.  Raises Nf4Error (status NF4_ERR_SCRATCH) when the shape needs more
+    scratch than that array holds."""
+    import torch
+    M, N = grad_out.shape
+    K = codes.shape[1] * 2
+    _require(grad_out, torch.float32, (M, N), "grad_out")
+    _require(scales, torch.float32, (N, K // 64), "scales")
+    _require(codes, torch.uint8, (N, K // 2), "codes")
+    _require(out, torch.float32, (M, K), "out")
+    _check(_lib.nf4_grad_a_noalloc(_ptr(grad_out), _ptr(scales), _ptr(codes), _ptr(out), M, N, K,
+                                   _stream_handle(stream)), "nf4_grad_a_noalloc")
     return out
 
 

@@ -50,6 +50,20 @@ int nf4_grad_a(const float* grad_out, const float* scales, const uint8_t* codes,
   return from_hip(nf4::launch_grad_a(grad_out, scales, codes, grad_a, M, N, K, stream));
 }
 
+int nf4_grad_a_noalloc(const float* grad_out, const float* scales, const uint8_t* codes, float* grad_a, int64_t M,
+                       int64_t N, int64_t K, hipStream_t stream) {
+  static_assert(nf4::kNoallocScratchBytes == (size_t)NF4_NOALLOC_SCRATCH_BYTES, "scratch size as declared");
+  if (!dims_ok(M, N) || !dims_ok(N, K) || !dims_ok(M, K) || (K % 64) != 0) return NF4_ERR_SHAPE;
+  if (M == 0 || K == 0) return NF4_OK;
+  if (grad_a == nullptr) return NF4_ERR_NULL;
+  if (N > 0 && (grad_out == nullptr || scales == nullptr || codes == nullptr)) return NF4_ERR_NULL;
+  if (!aligned16(grad_a) || (N > 0 && (!aligned16(grad_out) || !aligned16(scales) || !aligned16(codes))))
+    return NF4_ERR_ALIGN;
+  if (nf4::grad_a_workspace_bytes(nf4::plan_grad_a(M, N, K), M, N, K) > nf4::noalloc_scratch_capacity())
+    return NF4_ERR_SCRATCH;
+  return from_hip(nf4::launch_grad_a_noalloc(grad_out, scales, codes, grad_a, M, N, K, stream));
+}
+
 int nf4_dequant(const float* scales, const uint8_t* codes, float* w_out, int64_t N, int64_t K, hipStream_t stream) {
   if (!dims_ok(N, K) || (K % 64) != 0) return NF4_ERR_SHAPE;
   if (N == 0 || K == 0) return NF4_OK;
@@ -186,6 +200,7 @@ const char* nf4_status_string(int status) {
     case NF4_ERR_ALIGN: return "pointer not 16-byte aligned";
     case NF4_ERR_HIP: return "HIP launch, allocation or synchronisation failed";
     case NF4_ERR_CAPTURE: return "the stream's workspace would have to grow during HIP graph capture";
+    case NF4_ERR_SCRATCH: return "the call needs more scratch than nf4_grad_a_noalloc's static buffer holds";
     default: return "unknown nf4 status";
   }
 }

@@ -47,9 +47,32 @@ constexpr int kWsCounters = 4096;
 hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** out, uint32_t** counters = nullptr);
 hipError_t release_workspaces();
 
-// Launch a given plan (its partials and fragments in the stream's workspace).
+// Caller-provided scratch in place of the stream's workspace: `bytes` at
+// `base` for the plan's partials and fragments, and kWsCounters arrival
+// counters (zero between calls).
+struct FixedScratch {
+  char* base;
+  size_t bytes;
+  uint32_t* counters;
+};
+
+// Launch a given plan; its partials and fragments go to the stream's
+// workspace, or to `fixed` when given (nothing is allocated then).
 hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const float* scales, const uint8_t* codes,
-                              float* grad_a, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                              float* grad_a, int64_t M, int64_t N, int64_t K, hipStream_t stream,
+                              const FixedScratch* fixed = nullptr);
+// Bytes of workspace a plan needs beyond the arrival counters.
+size_t grad_a_workspace_bytes(const GradAPlan& p, int64_t M, int64_t N, int64_t K);
+
+// nf4_grad_a without any allocation: nf4_grad_a's plan with its scratch in a
+// static device array of kNoallocScratchBytes per GPU (the arrival counters,
+// then noalloc_scratch_capacity() bytes).  hipErrorOutOfMemory (nothing
+// enqueued) when the plan needs more.
+constexpr size_t kNoallocScratchBytes = (size_t)128 << 20;
+size_t noalloc_scratch_capacity();
+hipError_t launch_grad_a_noalloc(const float* grad_out, const float* scales, const uint8_t* codes, float* grad_a,
+                                 int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 // Wide tile kernel (nf4_grad_a_wide.hip): usable when N % 64 == 0 and the
 // operands have 32-bit byte offsets; its tile is wide_tile_rows() x
 // wide_tile_cols() (512 x 128).

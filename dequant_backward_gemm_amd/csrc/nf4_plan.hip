@@ -286,8 +286,63 @@ static PlanWorkspace plan_workspace(const GradAPlan& p, int64_t M, int64_t N, in
   return w;
 }
 
+size_t grad_a_workspace_bytes(const GradAPlan& p, int64_t M, int64_t N, int64_t K) {
+  return plan_workspace(p, M, N, K).total();
+}
+
+// ---- Fixed scratch of nf4_grad_a_noalloc ----------------------------------
+// A static device array (each GPU the library runs on holds its own copy until
+// the process ends).  Host code never passes its name to a kernel: the name is
+// a host-side stand-in, so its device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is
+// used.  The first kWsCounters dwords are the streaming kernel's arrival
+// counters, zeroed by a fill kernel on the first call's stream; kernels leave
+// them at zero.  Every call on a GPU shares the array.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mutex;
+std::vector<void*> g_scratch_ptr;  // device address of `scratch`, per device (null until set up)
+}  // namespace
+
+static hipError_t noalloc_scratch(hipStream_t stream, FixedScratch* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    // the counters start at zero (a kernel, in this stream's order)
+    e = launch_fill_zero(1, static_cast<float*>(ptr), (int64_t)kWsCounters * 4 / 16, stream);
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  constexpr size_t kHeader = (size_t)kWsCounters * sizeof(uint32_t);
+  out->counters = static_cast<uint32_t*>(g_scratch_ptr[dev]);
+  out->base = static_cast<char*>(g_scratch_ptr[dev]) + kHeader;
+  out->bytes = kNoallocScratchBytes - kHeader;
+  return hipSuccess;
+}
+
+size_t noalloc_scratch_capacity() { return kNoallocScratchBytes - (size_t)kWsCounters * sizeof(uint32_t); }
+
+hipError_t launch_grad_a_noalloc(const float* grad_out, const float* scales, const uint8_t* codes, float* grad_a,
+                                 int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const GradAPlan p = plan_grad_a(M, N, K);
+  if (grad_a_workspace_bytes(p, M, N, K) > noalloc_scratch_capacity()) return hipErrorOutOfMemory;
+  FixedScratch fs{};
+  hipError_t e = noalloc_scratch(stream, &fs);
+  if (e != hipSuccess) return e;
+  return launch_grad_a_plan(p, grad_out, scales, codes, grad_a, M, N, K, stream, &fs);
+}
+
 hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const float* scales, const uint8_t* codes,
-                              float* grad_a, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                              float* grad_a, int64_t M, int64_t N, int64_t K, hipStream_t stream,
+                              const FixedScratch* fixed) {
   const uint32_t* c32 = reinterpret_cast<const uint32_t*>(codes);
   if (p.kernel == 2) return launch_fill_zero(p.grid, grad_a, M * K / 4, stream);
   float* dst = grad_a;
@@ -303,9 +358,15 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
     const PlanWorkspace w = plan_workspace(p, M, N, K);
     if (w.total() > 0) {
       char* base = nullptr;
-      hipError_t e = stream_workspace(stream, w.total(), reinterpret_cast<void**>(&base),
-                                      fused_reduce ? &counters : nullptr);
-      if (e != hipSuccess) return e;
+      if (fixed != nullptr) {
+        if (w.total() > fixed->bytes) return hipErrorOutOfMemory;
+        base = fixed->base;
+        if (fused_reduce) counters = fixed->counters;
+      } else {
+        hipError_t e = stream_workspace(stream, w.total(), reinterpret_cast<void**>(&base),
+                                        fused_reduce ? &counters : nullptr);
+        if (e != hipSuccess) return e;
+      }
       if (w.part) ws = reinterpret_cast<float*>(base);
       if (w.frag) frags = base + w.part_al;
       if (w.bfrag) bfrags = base + w.part_al + w.frag_al;

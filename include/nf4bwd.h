@@ -79,7 +79,8 @@ typedef enum nf4_status {
   NF4_ERR_SHAPE = 2,  /* negative size, K % 64 != 0, or a size over 2^31-1 */
   NF4_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned */
   NF4_ERR_HIP = 4,    /* a HIP launch, allocation or synchronisation failed */
-  NF4_ERR_CAPTURE = 5 /* the stream's workspace would have to grow during graph capture */
+  NF4_ERR_CAPTURE = 5, /* the stream's workspace would have to grow during graph capture */
+  NF4_ERR_SCRATCH = 6  /* nf4_grad_a_noalloc: the call needs more than its static scratch */
 } nf4_status;
 
 /*
@@ -104,6 +105,27 @@ typedef enum nf4_status {
  */
 int nf4_grad_a(const float* grad_out, const float* scales, const uint8_t* codes,
                float* grad_a, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
+ * nf4_grad_a_noalloc -- nf4_grad_a for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, layout, contract and launch plan as
+ * nf4_grad_a, and bitwise the same results; it allocates nothing (no
+ * hipMalloc, hipMallocAsync or hipFree, and no stream workspace).  Its
+ * kernels' scratch -- split partials, arrival counters, fp16 A fragments --
+ * lives in one static device array of NF4_NOALLOC_SCRATCH_BYTES (128 MiB),
+ * which every GPU the library runs on holds until the process ends; the first
+ * call on a GPU looks up its address there and clears its counters with a
+ * kernel on `stream`.  A shape whose plan needs more than that (the plan's
+ * partials and fragments, e.g. 2 * 16*ceil(M/16) * N bytes of fragments for
+ * large M) returns NF4_ERR_SCRATCH and enqueues nothing.  Every call on one
+ * GPU shares the array and leaves it as the next call needs it: calls that
+ * overlap on one GPU (on different streams, or a graph replay beside another
+ * call) race and must not be issued.
+ */
+#define NF4_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+int nf4_grad_a_noalloc(const float* grad_out, const float* scales, const uint8_t* codes,
+                       float* grad_a, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /*
  * nf4_dequant -- w_out[n][k] = fl32(scales[n][k/64] * NF4[code(n,k)]), fp32

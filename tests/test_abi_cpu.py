@@ -43,9 +43,10 @@ def test_library_exports_every_declared_symbol(nb):
 
 
 def test_status_strings(nb):
-    for s in range(6):
+    for s in range(7):
         assert nb.status_string(s) and "unknown" not in nb.status_string(s)
     assert "capture" in nb.status_string(nb.NF4_ERR_CAPTURE)
+    assert "scratch" in nb.status_string(nb.NF4_ERR_SCRATCH)
     assert "unknown" in nb.status_string(99)
 
 
