@@ -25,6 +25,8 @@ import os
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libnf4bwd.so")
+# the race-check build (every LDS phase separated by an extra barrier); tests only
+BARRIER_LIB_PATH = os.path.join(_PKG_DIR, "libnf4bwd_barriers.so")
 
 NF4_OK, NF4_ERR_NULL, NF4_ERR_SHAPE, NF4_ERR_ALIGN, NF4_ERR_HIP, NF4_ERR_CAPTURE, NF4_ERR_SCRATCH = 0, 1, 2, 3, 4, 5, 6
 NOALLOC_SCRATCH_BYTES = 128 << 20
@@ -51,10 +53,11 @@ class Nf4Error(RuntimeError):
         super().__init__(f"{what}: {status_string(status)} (status {status})")
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load a build of the C-ABI library (the release one by default) with its argument types declared."""
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python dequant_backward_gemm_amd/build.py` "
+            f"{path} is missing: build it with `python dequant_backward_gemm_amd/build.py` "
             "(hipcc, gfx950). There is no CPU fallback.")
     # One HIP runtime per process: PyTorch ships its own libamdhip64, and the
     # library must bind to that copy, since it works on torch's memory and
@@ -64,7 +67,7 @@ def _load() -> ctypes.CDLL:
         import torch  # noqa: F401
     except ImportError:
         pass
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.nf4_grad_a.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     lib.nf4_grad_a.restype = ctypes.c_int
@@ -96,7 +99,7 @@ def _load() -> ctypes.CDLL:
     return lib
 
 
-_lib = _load()
+_lib = load_library(LIB_PATH)
 
 
 def status_string(status: int) -> str:

@@ -159,6 +159,7 @@ __global__ __launch_bounds__(512, 1) void nf4_forward_kernel(const void* __restr
     for (int s = 0; s < 2; ++s) {
       uint32_t lk[8];
       for_each_index(std::make_integer_sequence<int, 8>{}, [&](auto ec) { lk[decltype(ec)::value] = lookup(ec, x0[s], 0u); });
+      NF4_PHASE_BARRIER();
       u32x4 f;
 #pragma unroll
       for (int p = 0; p < 4; ++p) f[p] = lk[2 * p] | (lk[2 * p + 1] << 16);
@@ -215,6 +216,7 @@ __global__ __launch_bounds__(512, 1) void nf4_forward_kernel(const void* __restr
         if constexpr (t == 6 && s == 1) scn = load_scale(st + 3);
         if constexpr (t == 7 && s == 0) build_tables(sc, toff_build);
         __builtin_amdgcn_sched_barrier(0);
+        NF4_PHASE_BARRIER();  // race-check build: every tick's LDS accesses complete before the next
       });
     });
     __syncthreads();

@@ -167,6 +167,7 @@ __device__ __forceinline__ void forward_strip(const float* __restrict__ A, const
       for (int p = 0; p < 4; ++p) bf[p] = pack_half2_rne(d.sc[t] * lk[i & 1][2 * p], d.sc[t] * lk[i & 1][2 * p + 1]);
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(af), as_half8(bf), acc[t], 0, 0, 0);
     });
+    NF4_PHASE_BARRIER();  // race-check build: the step's A reads complete before the next step's stores
   };
 
   // The next step's loads are in flight while one is decoded (two named

@@ -172,6 +172,7 @@ __global__ __launch_bounds__(256, (RB == 1 ? 2 : 1)) void grad_a_tile_kernel(
       load_a(nb + 64 * (st + 1));
     }
     compute(buf);
+    NF4_PHASE_BARRIER();  // race-check build: the stage's fragment reads complete before the next decode
     if (more) {
       decode_store(buf ^ 1);
       convert_a();

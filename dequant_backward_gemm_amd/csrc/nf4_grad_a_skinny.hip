@@ -135,6 +135,7 @@ __device__ __forceinline__ void stream_strip(const float* __restrict__ G, const 
       lds_store_u32x4(smem, tbuild, w0);
       lds_store_u32x4(smem, tbuild + 16u, w1);
     }
+    NF4_WAVE_DRAIN();  // race-check build: the wave's tables are complete before anything reads them
     // grad_out of the k-step into the A layout
     u32x4 af;
     {
@@ -146,6 +147,7 @@ __device__ __forceinline__ void stream_strip(const float* __restrict__ G, const 
 #pragma unroll
       for (int p = 0; p < 4; ++p) h[p] = pack_half2_rne(g[2 * p], g[2 * p + 1]);
       lds_store_u32x4(smem, astore, h);
+      NF4_WAVE_DRAIN();
       af = lds_load_u32x4(smem, aread);
     }
     // decode (one table read per weight) and MFMA, tile by tile
@@ -172,6 +174,7 @@ __device__ __forceinline__ void stream_strip(const float* __restrict__ G, const 
       for (int p = 0; p < 4; ++p) b[p] = lk[t & 1][2 * p] | (lk[t & 1][2 * p + 1] << 16);
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(af), as_half8(b), acc[t], 0, 0, 0);
     });
+    NF4_WAVE_DRAIN();  // race-check build: the step's table reads complete before the next step's builds
   };
 
   // Wave w takes k-steps w, w + 8, ... (cnt of them); the next one's loads are

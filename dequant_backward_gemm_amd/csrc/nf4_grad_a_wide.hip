@@ -435,6 +435,7 @@ __device__ __forceinline__ void wide_tile(const void* __restrict__ Gv, const flo
     for_each_index(std::make_integer_sequence<int, 8>{}, [&](auto cc) {
       uint32_t lk[WC][2];
       lookup_col(cc, 0u, lk);
+      NF4_PHASE_BARRIER();
       store_col(cc, 0u, lk);
     });
     __syncthreads();
@@ -504,6 +505,7 @@ __device__ __forceinline__ void wide_tile(const void* __restrict__ Gv, const flo
           if constexpr (t == 7 && s == 0) build_tables(sc, toff_build);
         }
         __builtin_amdgcn_sched_barrier(0);
+        NF4_PHASE_BARRIER();  // race-check build: every tick's LDS accesses complete before the next
       });
     });
     __syncthreads();

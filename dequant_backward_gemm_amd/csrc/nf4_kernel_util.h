@@ -6,6 +6,31 @@
 
 #include "nf4_device.h"
 
+// Race-check build (NF4_EXTRA_BARRIERS defined): every kernel separates each
+// of its LDS phases with an extra barrier, so that no wave starts a phase
+// before all have finished the previous one; its results must equal the
+// release build's bit for bit.  NF4_PHASE_BARRIER() is a workgroup barrier and
+// sits only where every wave of the workgroup passes the same number of
+// times; NF4_WAVE_DRAIN() completes a wave's own LDS accesses (for phases on a
+// wave's private LDS area, in loops whose trip count differs between waves).
+#ifdef NF4_EXTRA_BARRIERS
+#define NF4_PHASE_BARRIER() __syncthreads()
+#define NF4_WAVE_DRAIN()                                                 \
+  do {                                                                   \
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");               \
+    __builtin_amdgcn_s_waitcnt(0xc07f); /* lgkmcnt(0) */                 \
+    __builtin_amdgcn_wave_barrier();                                     \
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");               \
+  } while (0)
+#else
+#define NF4_PHASE_BARRIER() \
+  do {                      \
+  } while (0)
+#define NF4_WAVE_DRAIN() \
+  do {                   \
+  } while (0)
+#endif
+
 namespace nf4 {
 
 // Consecutive workgroup ids are dispatched round-robin over the 8 XCDs.
