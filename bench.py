@@ -614,6 +614,8 @@ def main():
     ap.add_argument("--one", type=str, default=None, metavar="M,N,K",
                     help="only run nf4_grad_a on one shape (packed N(0, 0.02) weights, grad_out N(0, 1e-2)) "
                          "--steps times after --warmup calls, for counter collection; prints one JSON line")
+    ap.add_argument("--forced", type=str, default=None, metavar="KERNEL,RB,SPLITS",
+                    help="with --one: run nf4_grad_a_forced with this plan (kernel name as in the binding)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for scaling HBM byte counters) and exit")
     args = ap.parse_args()
@@ -637,17 +639,27 @@ def main():
         del w
         g = torch.empty((M, N), device="cuda").normal_(0.0, 1e-2, generator=gen)
         o = torch.empty((M, K), device="cuda")
+        if args.forced:
+            fk, frb, fsp = args.forced.split(",")
+
+            def call():
+                nb.grad_a_forced(g, s, c, fk, rb=int(frb), splits=int(fsp), out=o)
+            plan = {"forced": args.forced}
+        else:
+            def call():
+                nb.grad_a(g, s, c, out=o)
+            plan = nb.grad_a_plan(M, N, K)
         for _ in range(args.warmup):
-            nb.grad_a(g, s, c, out=o)
+            call()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.steps):
-            nb.grad_a(g, s, c, out=o)
+            call()
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / max(args.steps, 1)
-        print(json.dumps({"shape": [M, N, K], "plan": nb.grad_a_plan(M, N, K), "us_per_call": round(us, 2),
+        print(json.dumps({"shape": [M, N, K], "plan": plan, "us_per_call": round(us, 2),
                           "tflops": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 2)}), flush=True)
         return
     if args.unfused_configs:

@@ -31,7 +31,7 @@ BARRIER_LIB_PATH = os.path.join(PKG_DIR, "libnf4bwd_barriers.so")
 OBJ_DIR = os.path.join(PKG_DIR, "_build")
 
 SOURCES = ["nf4_abi.hip", "nf4_plan.hip", "nf4_dequant.hip", "nf4_pack.hip", "nf4_grad_a.hip",
-           "nf4_grad_a_wide.hip", "nf4_grad_a_skinny.hip", "nf4_forward.hip", "nf4_forward_skinny.hip", "rms_norm_bwd.hip"]
+           "nf4_grad_a_wide.hip", "nf4_grad_a_skinny.hip", "nf4_grad_a_lines.hip", "nf4_forward.hip", "nf4_forward_skinny.hip", "rms_norm_bwd.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -25,8 +25,9 @@ struct GradAPlan {
                  // 3 = wide (8 waves, tile 512 x 128, fp32 grad_out converted in the loop),
                  // 4 = stream (M <= 16),
                  // 5 = wide fed by fp16 A fragments from a conversion pass (tile 512 x 128),
-                 // 6 = unfused comparison path (fp16 weight pass, then a fragment-copy GEMM)
-  int rb;        // tile: 32-row blocks per wave; wide: 1
+                 // 6 = unfused comparison path (fp16 weight pass, then a fragment-copy GEMM),
+                 // 8 = line streaming (M <= 16, 256-column strips)
+  int rb;        // tile: 32-row blocks per wave; wide: 1; line streaming: rows decoded in registers
   int splits;    // number of N-chunks (1 = no workspace, no reduce launch)
   int n_chunk;   // rows of N per chunk
   int grid;      // workgroups of the main kernel
@@ -217,6 +218,20 @@ hipError_t launch_grad_a_stream_grouped(const StreamGroup& g, int grid, hipStrea
 hipError_t launch_grad_a_stream(int grid, const float* grad_out, const float* scales, const uint32_t* codes,
                                 float* dst, float* grad_a, uint32_t* counters, int M, int N, int K, int n_chunk,
                                 int tiles_k, int splits, hipStream_t stream);
+
+// Line-streaming kernel for M <= 16 (nf4_grad_a_lines.hip): 256-column strips
+// (whole 128-byte code lines), N-chunks of whole 16-row k-steps, one 8-wave
+// workgroup per CU; `vr` (0..4) of each lane's 4 rows are decoded
+// through the shared fp32 codebook, the rest through per-k-step fp16 tables.
+// Needs N % 4 == 0 (16-byte grad_out
+// rows) and 32-bit byte offsets.  With
+// splits > 1, dst holds the partials and, when `counters` is given, the last
+// workgroup of each strip sums them in split order into grad_a.
+constexpr int kLinesBK = 256;
+bool lines_kernel_supported(int64_t M, int64_t N, int64_t K);
+hipError_t launch_grad_a_lines(int vr, int grid, const float* grad_out, const float* scales, const uint32_t* codes,
+                               float* dst, float* grad_a, uint32_t* counters, int M, int N, int K, int n_chunk,
+                               int tiles_k, int splits, hipStream_t stream);
 
 // Kernel launchers of nf4_grad_a.hip (tile, skinny, split reduction, zero fill).
 hipError_t launch_grad_a_tile(int rb, int grid, const float* grad_out, const float* scales, const uint32_t* codes,

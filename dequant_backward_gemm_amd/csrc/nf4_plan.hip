@@ -240,6 +240,14 @@ bool make_plan(int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, 
     p.n_chunk = (int)chunk;
     p.splits = (int)cdiv(N, chunk);
     p.grid = (int)(cdiv(K, kStreamBK) * p.splits);
+  } else if (kernel == 8) {
+    if (!lines_kernel_supported(M, N, K) || rb < 0 || rb > 5) return false;
+    const int64_t chunk = cdiv(cdiv(N, splits), 16) * 16;
+    p.kernel = 8;
+    p.rb = rb;
+    p.n_chunk = (int)chunk;
+    p.splits = (int)cdiv(N, chunk);
+    p.grid = (int)(cdiv(K, kLinesBK) * p.splits);
   } else if (kernel == 5 || kernel == 6) {
     if (!wide_kernel_supported(M, N, K)) return false;
     const int64_t chunk = cdiv(cdiv(N, splits), 64) * 64;
@@ -352,7 +360,8 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
   uint32_t* counters = nullptr;
   // the streaming kernel sums its own split partials (per-strip arrival counters;
   // 32-bit byte offsets into the partials)
-  const bool fused_reduce = p.kernel == 4 && p.splits > 1 && cdiv(K, kStreamBK) <= kWsCounters &&
+  const bool fused_reduce = (p.kernel == 4 || p.kernel == 8) && p.splits > 1 &&
+                            cdiv(K, p.kernel == 8 ? kLinesBK : kStreamBK) <= kWsCounters &&
                             (uint64_t)p.splits * (uint64_t)M * (uint64_t)K * 4 < (1ull << 32);
   {
     const PlanWorkspace w = plan_workspace(p, M, N, K);
@@ -380,6 +389,9 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
   } else if (p.kernel == 4) {
     e = launch_grad_a_stream(p.grid, grad_out, scales, c32, dst, grad_a, counters, (int)M, (int)N, (int)K, p.n_chunk,
                              (int)cdiv(K, kStreamBK), p.splits, stream);
+  } else if (p.kernel == 8) {
+    e = launch_grad_a_lines(p.rb, p.grid, grad_out, scales, c32, dst, grad_a, counters, (int)M, (int)N, (int)K,
+                            p.n_chunk, (int)cdiv(K, kLinesBK), p.splits, stream);
   } else if (p.kernel == 6) {
     e = launch_grad_a_unfused(p.grid, grad_out, frags, bfrags, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
                               (int)cdiv(M, wide_tile_rows()), (int)cdiv(K, wide_tile_cols()), stream);

@@ -173,7 +173,12 @@ int nf4_grad_a_plan(int64_t M, int64_t N, int64_t K, int* out5);
  * unfused comparison path: the weights dequantised to fp16 by a separate pass
  * (2 * N * 128*ceil(K/128) bytes of workspace), then the kernel-5 GEMM
  * reading them instead of decoding (same requirements, bitwise the same
- * result as kernel 5); `splits` = requested number of N-chunks (rounded so
+ * result as kernel 5), kernel 8 = line streaming for M <= 16 (requires
+ * N % 4 == 0 and grad_out and the codes below 2 GiB; 256-column strips of
+ * whole code lines; `rb` 0..4 = rows of each lane's 4 decoded in registers
+ * from byte planes, the rest by 16-bit table reads, 5 = one row through the
+ * shared codebook: every `rb` gives bitwise the same result); `splits` =
+ * requested number of N-chunks (rounded so
  * that every chunk but the last is a whole number of stages).  Same contract
  * and results-to-bound as nf4_grad_a; NF4_ERR_SHAPE if the forced plan does
  * not fit the shape.

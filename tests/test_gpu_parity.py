@@ -656,3 +656,47 @@ def test_grad_a_rejects_bad_arguments_on_device(lib):
     assert st == lib.NF4_ERR_SHAPE
     with pytest.raises(lib.Nf4Error):
         lib.grad_a_forced(torch.zeros((17, N), device="cuda"), s, b, "skinny")   # skinny needs M <= 16
+
+
+# ------------------------------------------- line streaming (M <= 16, 256-column strips, hybrid decode)
+
+@pytest.mark.parametrize("vr", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("splits", [1, 3, 9])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (2, 36, 192), (7, 260, 320), (16, 2048, 640), (9, 5000, 128),
+                                   (16, 28, 64), (16, 300, 1088)])
+def test_grad_a_lines_ragged(lib, vr, splits, M, N, K):
+    """Line-streaming kernel, every split of its rows between register (byte-plane) decode and 16-bit table
+    reads, and one row through the shared codebook (variant 5): ragged M, N inside a 16-row k-step, K % 256
+    != 0 (the last strip part-empty), N-chunk partials summed in the kernel (the last workgroup's threads
+    sharing an output when there are few)."""
+    g, s, b = random_inputs(M, N, K, seed=M + 5 * N + 3 * K + 7 * splits + vr)
+    check_grad_a(lib, g, s, b, M, N, K, kernel="lines", rb=vr, splits=splits,
+                 what=f"lines vr{vr} s{splits} {M}x{N}x{K}")
+
+
+def test_grad_a_lines_decode_paths_agree_bitwise(lib):
+    """The register decode (byte-plane v_perm lookups) and the LDS decode produce the same fp16 weights, so
+    every split of the rows between them gives bitwise the same result; one-hot rows give fp16(dequant)
+    rows exactly on both paths; repeated calls with other split counts leave the arrival counters at zero."""
+    M, N, K = 16, 3000, 768
+    g, s, b = random_inputs(M, N, K, seed=91)
+    gd, sd, bd = dev(g), dev(s), dev(b)
+    base = host(lib.grad_a_forced(gd, sd, bd, "lines", rb=0, splits=4))
+    for vr in (1, 2, 3, 4, 5):
+        for splits in (4, 1, 7):
+            r = host(lib.grad_a_forced(gd, sd, bd, "lines", rb=vr, splits=splits))
+            if splits == 4:
+                assert np.array_equal(r.view(np.uint32), base.view(np.uint32)), vr
+            else:
+                ref, S = oracle.grad_a(g, s, b, M, N, K)
+                assert_within_bound(r, ref, S, f"lines vr{vr} s{splits}")
+    # one-hot rows: grad_A row m = fp16(W[n_m][:]) exactly
+    picks = [0, 1, 17, 255, 256, 1023, 2999, 5, 6, 7, 8, 9, 10, 11, 12, 13]
+    oh = np.zeros((M, N), dtype=np.float32)
+    for m, n in enumerate(picks):
+        oh[m, n] = 1.0
+    w16 = oracle.dequant(s, b, N, K).astype(np.float16).astype(np.float32)
+    for vr in (0, 2, 4, 5):
+        r = host(lib.grad_a_forced(dev(oh), sd, bd, "lines", rb=vr, splits=3))
+        for m, n in enumerate(picks):
+            assert np.array_equal(r[m].view(np.uint32), w16[n].view(np.uint32)), (vr, m, n)
