@@ -119,10 +119,10 @@ def kernel_name_for(plan, N=None):
     if plan["kernel"] == "wide16":
         # two kernels per call: the fp16 A-fragment pass, then the wide kernel reading the fragments
         return "grad_out_frag_kernel<false>+grad_a_wide_kernel<1, 3, false>"
+    if plan["kernel"] == "mid":
+        return "grad_out_frag_kernel<false>+grad_a_mid_kernel<%d>" % plan["rb"]
     if plan["kernel"] == "stream":
         return "grad_a_stream_kernel<true>" if N is not None and N % 4 == 0 else "grad_a_stream_kernel<false>"
-    if plan["rb"] == 2 and N is not None and N % 64 == 0:
-        return "grad_a_tile_fast_kernel"
     return "grad_a_tile_kernel<%d>" % plan["rb"]
 
 
@@ -314,7 +314,7 @@ def per_config_unfused(torch, nb):
         gstd = 1.0 if shp.M <= 16 else 1e-2
         fused, _, _, _ = time_config(torch, nb, shp.M, shp.N, shp.K, seed=i, g_std=gstd)
         plan = nb.grad_a_plan(shp.M, shp.N, shp.K)
-        sp = plan["splits"] if plan["kernel"] in ("wide", "wide16") else unfused_splits(shp.M, shp.N, shp.K)
+        sp = plan["splits"] if plan["kernel"] in ("wide", "wide16", "mid") else unfused_splits(shp.M, shp.N, shp.K)
         unf, _, _, nsets = time_config(torch, nb, shp.M, shp.N, shp.K, seed=i, g_std=gstd, op="unfused", splits=sp)
         fl = 2.0 * shp.M * shp.N * shp.K
         out[shp.name] = {"M": shp.M, "N": shp.N, "K": shp.K, "fused_us": round(fused * 1e6, 2),

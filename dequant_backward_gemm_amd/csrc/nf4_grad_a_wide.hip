@@ -385,6 +385,8 @@ __device__ __forceinline__ void wide_tile(const void* __restrict__ Gv, const flo
     for (int rb = 0; rb < 4; ++rb) af[rb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, voff_f[rb], soff, 0));
   };
   constexpr int NAB = AF ? AF + 1 : 1;  // fragment buffers in the ring
+  // buffer (2 P + s) % NAB must hold k-step 2 st + s for either stage parity P = st % 2
+  static_assert(4 % NAB == 0, "fragment ring of 1, 2 or 4 buffers");
   u32x4 afr[NAB][4];
 
   // fragment copy (BCOPY): thread tid moves bytes 16 tid and 8192 + 16 tid of a stage's 16 KiB
@@ -549,6 +551,286 @@ __device__ __forceinline__ void wide_tile(const void* __restrict__ Gv, const flo
   }
 }
 
+// acc += A . B, one 16x16x32 fp16 MFMA with the accumulator in AGPRs, as
+// inline assembly: left to itself the compiler keeps some of the mid-size
+// tile's accumulators in VGPRs and copies them between the two files around
+// the MFMAs.  The hardware does not interlock every dependency of an MFMA,
+// and the compiler inserts the required wait states only around MFMAs it
+// issued itself, so the rules that keep this safe are local: the operands
+// come from loads only (no VALU instruction writes them), an MFMA reading as
+// SrcC the exact AGPRs the previous MFMA of the same shape wrote needs no
+// wait states, and the accumulators are zeroed and read back only behind
+// explicit waits with scheduling fences (below).  tests/test_asm_hazards.py
+// scans the compiled code of every kernel that uses it for a VALU write of an
+// MFMA operand within two wait states before the MFMA and for a read of an
+// MFMA result within 19 wait states after it.
+__device__ __forceinline__ void mfma_acc(floatx4_t& acc, const u32x4& a, const u32x4& b) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Mid-size tile: 256 x 128 with four waves (256 threads) and two workgroups
+// per CU, for problems whose 512 x 128 tiles leave CUs idle or end in a thin
+// last round.  Wave w owns rows 64w .. 64w + 63 (four 16-row blocks x eight
+// MFMA tiles, 128 accumulators per lane, as in the eight-wave kernel), fed by
+// the same fp16 A fragments.  The decode and table roles and every LDS layout
+// are those of the eight-wave kernel, each lane playing two of its lanes
+// (waves w and w + 4), so the B operands and the reduction order are the same
+// and the results are bitwise equal to the 512 x 128 kernel's.
+template <int AF>
+__device__ __forceinline__ void mid_tile(const void* __restrict__ Gv, const float* __restrict__ S,
+                                         const uint32_t* __restrict__ C32, int M, int N, int K, int tiles_k, int tile,
+                                         int nb, int ne, float* __restrict__ dst, int ld) {
+  // buffer (2 P + s) % (AF + 1) must hold k-step 2 st + s for either stage parity P = st % 2
+  static_assert(AF == 1 || AF == 3, "fragment prefetch depth 1 or 3");
+  using Cfg = WideCfg<1>;
+  constexpr int BK = Cfg::BK, KB = Cfg::KB;
+  constexpr uint32_t kTabStage = Cfg::kTabStage, kFragStage = Cfg::kFragStage;
+  constexpr int RB = 4;        // 16-row blocks per wave
+  constexpr int BM = 64 * RB;  // tile rows: four waves
+  __shared__ __attribute__((aligned(16))) uint32_t smem[Cfg::kLds / 4];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+
+  const int kt = tile % tiles_k;
+  const int mt = tile / tiles_k;
+  const int m0 = mt * BM, k0 = kt * BK;
+  const int nst = (ne - nb) >> 6;
+
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(C32, (uint32_t)((size_t)N * (size_t)K / 2));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(S, (uint32_t)((size_t)N * (size_t)(K / 64) * 4));
+  const int mpad = (M + 15) & ~15;
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(Gv, (uint32_t)((size_t)mpad * (size_t)N * 2));
+  const uint32_t crow = (uint32_t)K / 2;   // bytes per code row
+  const uint32_t srow = (uint32_t)K / 16;  // bytes per scale row
+  auto stage_row = [&](int st) { return (uint32_t)(nb + 64 * min(st, nst - 1)); };
+
+  // ---- MFMA role: rows 128*wave + 16*rb + ci of the tile ----
+  const uint32_t rbase = Cfg::kFragBase + 16u * lane;
+  // fragment (mb, ks) of row block rb at ((mb * N/32 + ks) * 64 + lane) * 16,
+  // mb = (m0 + 128 wave) / 16 + rb; blocks past the padded M read zero
+  const uint32_t fstride = (uint32_t)(N / 32) * 1024u;  // bytes between row blocks
+  const uint32_t voff_f = ((uint32_t)((m0 + 16 * RB * wave) / 16) * (uint32_t)(N / 32) * 64u + (uint32_t)lane) * 16u;
+
+  // ---- decode role: the eight-wave kernel's waves w and w + 4 (k-steps 0 and 1) ----
+  const int p = lane & 3, dl = lane >> 2;
+  uint32_t cvoff[2], tb[2][2], wb[2];
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const int vw = wave + 4 * v;
+    const int nr0 = 32 * (vw >> 2) + 16 * (p >> 1) + 4 * (vw & 3) + 2 * (p & 1);
+    cvoff[v] = (uint32_t)nr0 * crow + (uint32_t)(k0 / 2 + 4 * dl);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) tb[v][r] = Cfg::kTabBase + table_pos<KB>((uint32_t)((nr0 + r) * KB + (dl >> 3))) * 32u;
+    wb[v] = Cfg::kFragBase + (uint32_t)(vw >> 2) * 8192u + (uint32_t)(dl + 16 * (vw & 3)) * 16u + 4u * (uint32_t)p;
+  }
+  // ---- table role: slots tid / 4 and tid / 4 + 64, levels 4 * (tid % 4) .. + 3 ----
+  const int qq = tid & 3;
+  uint32_t svoff[2], twaddr[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int sl = (tid >> 2) + 64 * u;
+    svoff[u] = (uint32_t)(sl / KB) * srow + 4u * (uint32_t)(k0 / 64 + sl % KB);
+    twaddr[u] = Cfg::kTabBase + table_pos<KB>((uint32_t)sl) * 32u + 8u * qq;
+  }
+  float lv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lv[i] = kLevels[4 * qq + i];
+
+  floatx4_t acc[RB][8];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[rb][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  // the zeroing VALU writes must be two wait states ahead of the first MFMA
+  // that reads them as its accumulator input
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 1" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  auto load_codes = [&](int st, uint32_t (&x)[2][2]) {
+    const uint32_t r0 = stage_row(st);
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      x[v][0] = __builtin_amdgcn_raw_buffer_load_b32(rc, cvoff[v], r0 * crow, 0);
+      x[v][1] = __builtin_amdgcn_raw_buffer_load_b32(rc, cvoff[v], (r0 + 1) * crow, 0);
+    }
+  };
+  auto load_scales = [&](int st, float (&sc)[2]) {
+    const uint32_t r0 = stage_row(st);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      sc[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, svoff[u], r0 * srow, 0));
+  };
+  auto build_tables = [&](const float (&sc)[2], uint32_t toff) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      u32x2 w;
+      w[0] = pack_half2_rne(sc[u] * lv[0], sc[u] * lv[1]);
+      w[1] = pack_half2_rne(sc[u] * lv[2], sc[u] * lv[3]);
+      lds_store_u32x2(smem, twaddr[u] + toff, w);
+    }
+  };
+  uint32_t y[2][2], z[2][2];
+  auto prep = [&](const uint32_t (&x)[2][2]) {
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        y[v][r] = (x[v][r] << 1) & 0x1E1E1E1Eu;
+        z[v][r] = (x[v][r] >> 3) & 0x1E1E1E1Eu;
+      }
+  };
+  // decode of column c for both roles: four table reads, then (later) two packed stores
+  auto lookup_col = [&](auto cc, uint32_t toff, uint32_t (&lk)[2][2]) {
+    constexpr int c = decltype(cc)::value;
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const uint32_t s0 = (c & 1) ? z[v][0] : y[v][0];
+      const uint32_t s1 = (c & 1) ? z[v][1] : y[v][1];
+      lk[v][0] = lds_load_u16(smem, add_byte<(c >> 1)>(tb[v][0], s0) + toff);
+      lk[v][1] = lds_load_u16(smem, add_byte<(c >> 1)>(tb[v][1], s1) + toff);
+    }
+  };
+  auto store_col = [&](auto cc, uint32_t foff, const uint32_t (&lk)[2][2]) {
+    constexpr int c = decltype(cc)::value;
+#pragma unroll
+    for (int v = 0; v < 2; ++v) lds_store_u32(smem, wb[v] + foff + (uint32_t)(c * 1024), lk[v][0] | (lk[v][1] << 16));
+  };
+  // fp16 A fragments of k-step j of the chunk (j = 2 * stage + s), 8 row blocks
+  auto load_af = [&](int j, u32x4 (&af)[RB]) {
+    const uint32_t soff = (stage_row(j >> 1) / 32u + (uint32_t)(j & 1)) * 1024u;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      af[rb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, voff_f, soff + (uint32_t)rb * fstride, 0));
+  };
+  constexpr int NAB = AF + 1;  // fragment buffers in the ring
+  u32x4 afr[NAB][RB];
+
+  uint32_t xc[2][2];  // codes of the stage decoded during the current one
+  float sc[2];        // scales of the tables built during the current stage
+
+  // Prologue: tables of stages 0 and 1, stage 0 decoded into fragment buffer 0.
+  {
+    float s0[2], s1[2];
+    uint32_t x0[2][2];
+    load_scales(0, s0);
+    load_scales(1, s1);
+    load_codes(0, x0);
+    load_codes(1, xc);
+#pragma unroll
+    for (int j = 0; j < AF; ++j) load_af(j, afr[j]);
+    load_scales(2, sc);
+    build_tables(s0, 0);
+    build_tables(s1, kTabStage);
+    __syncthreads();
+    prep(x0);
+    for_each_index(std::make_integer_sequence<int, 8>{}, [&](auto cc) {
+      uint32_t lk[2][2];
+      lookup_col(cc, 0u, lk);
+      NF4_PHASE_BARRIER();
+      store_col(cc, 0u, lk);
+    });
+    __syncthreads();
+  }
+
+  // One stage: MFMAs on fragment buffer P, decode of stage st+1 into buffer
+  // P^1 with tables P^1, tables of stage st+2 into table buffer P.  Per
+  // k-step, eight ticks (one MFMA tile each, eight row blocks): B fragments
+  // read three ticks ahead through a ring of four; the decode of columns
+  // 4s .. 4s+3 of the next stage and the per-stage extras spread over them.
+  auto stage = [&](int st, auto par) {
+    constexpr uint32_t P = decltype(par)::value;
+    constexpr uint32_t toff_dec = (P ^ 1u) * kTabStage, toff_build = P * kTabStage;
+    constexpr uint32_t frd = P * kFragStage, fwr = (P ^ 1u) * kFragStage;
+    uint32_t xn[2][2];
+    float scn[2];
+    prep(xc);
+    for_each_index(std::make_integer_sequence<int, 2>{}, [&](auto sc_) {
+      constexpr int s = decltype(sc_)::value;
+      constexpr int c0 = 4 * s;
+      constexpr int b = (2 * (int)P + s) % NAB;
+      load_af(2 * st + s + AF, afr[(b + AF) % NAB]);
+      __builtin_amdgcn_sched_barrier(0);
+      auto read_b = [&](int t) { return lds_load_u32x4(smem, rbase + frd + (uint32_t)((s * 8 + t) * 1024)); };
+      u32x4 bf[4];
+      bf[0] = read_b(0);
+      bf[1] = read_b(1);
+      bf[2] = read_b(2);
+      uint32_t lk[2][2][2];
+      __builtin_amdgcn_sched_barrier(0);
+      for_each_index(std::make_integer_sequence<int, 8>{}, [&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) mfma_acc(acc[rb][t], afr[b][rb], bf[t % 4]);
+        if constexpr (t + 3 < 8) bf[(t + 3) % 4] = read_b(t + 3);
+        if constexpr (t >= 2 && t < 6) store_col(std::integral_constant<int, c0 + t - 2>{}, fwr, lk[t & 1]);
+        if constexpr (t < 4) lookup_col(std::integral_constant<int, c0 + t>{}, toff_dec, lk[t & 1]);
+        if constexpr (t == 6 && s == 0) load_codes(st + 2, xn);
+        if constexpr (t == 6 && s == 1) load_scales(st + 3, scn);
+        if constexpr (t == 7 && s == 0) build_tables(sc, toff_build);
+        __builtin_amdgcn_sched_barrier(0);
+        NF4_PHASE_BARRIER();  // race-check build: every tick's LDS accesses complete before the next
+      });
+    });
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      xc[v][0] = xn[v][0];
+      xc[v][1] = xn[v][1];
+      sc[v] = scn[v];
+    }
+  };
+
+  int st = 0;
+  for (; st + 1 < nst; st += 2) {
+    stage(st, std::integral_constant<uint32_t, 0>{});
+    stage(st + 1, std::integral_constant<uint32_t, 1>{});
+  }
+  if (st < nst) stage(st, std::integral_constant<uint32_t, 0>{});
+
+  // The MFMAs above are issued as inline assembly (accumulators pinned to
+  // AGPRs), which the compiler's hazard tracking does not see: wait out the
+  // last MFMAs' write-back before the accumulators are read, with scheduling
+  // fences so that no read moves above the wait.
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  // 16x16 accumulator layout: lane (ci, q), register r -> row 4*q + r, column ci.
+  const int ci = lane & 15, q = lane >> 4;
+  const int col = k0 + 8 * ci;
+  if (col < K) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + 16 * RB * wave + 16 * rb + 4 * q + r;
+        if (row < M) {
+          const floatx4 lo = {acc[rb][0][r], acc[rb][1][r], acc[rb][2][r], acc[rb][3][r]};
+          const floatx4 hi = {acc[rb][4][r], acc[rb][5][r], acc[rb][6][r], acc[rb][7][r]};
+          floatx4* o = reinterpret_cast<floatx4*>(dst + (size_t)row * (size_t)ld + col);
+          o[0] = lo;
+          o[1] = hi;
+        }
+      }
+    }
+  }
+}
+
+template <int AF>
+__global__ __launch_bounds__(256, 2) void grad_a_mid_kernel(const void* __restrict__ frags, const float* __restrict__ S,
+                                                            const uint32_t* __restrict__ C32, float* __restrict__ out,
+                                                            int M, int N, int K, int n_chunk, int tiles_m,
+                                                            int tiles_k) {
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int tiles = tiles_m * tiles_k;
+  const int split = logical / tiles;
+  const int nb = split * n_chunk;
+  mid_tile<AF>(frags, S, C32, M, N, K, tiles_k, logical % tiles, nb, min(N, nb + n_chunk),
+               out + (size_t)split * (size_t)M * (size_t)K, K);
+}
+
 // One tile over one N-chunk per workgroup; the chunk index is the slowest
 // part of the logical index and selects the partial-sum matrix it writes.
 template <int WC, int AF, bool BCOPY = false>
@@ -645,6 +927,20 @@ hipError_t launch_frag_pass(const float* src, void* frags, int rows, int cols, b
   else
     hipLaunchKernelGGL(grad_out_frag_kernel<false>, dim3(pgrid), dim3(256), 0, stream, src, static_cast<u32x4*>(frags),
                        rows, cols, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_a_mid_frag(int af, int grid, const float* grad_out, void* frags, const float* scales,
+                                  const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,
+                                  int tiles_k, hipStream_t stream) {
+  hipError_t e = launch_frag_pass(grad_out, frags, M, N, /*natural=*/false, stream);
+  if (e != hipSuccess) return e;
+  if (af == 1)
+    hipLaunchKernelGGL(grad_a_mid_kernel<1>, dim3(grid), dim3(256), 0, stream, frags, scales, codes, dst, M, N, K,
+                       n_chunk, tiles_m, tiles_k);
+  else
+    hipLaunchKernelGGL(grad_a_mid_kernel<3>, dim3(grid), dim3(256), 0, stream, frags, scales, codes, dst, M, N, K,
+                       n_chunk, tiles_m, tiles_k);
   return hipGetLastError();
 }
 

@@ -182,8 +182,8 @@ GradAPlan plan_grad_a(int64_t M, int64_t N, int64_t K) {
       const double t_unit = (double)BM * (double)BK * (double)chunk * 2.0 / (cu_rate * eff / per_cu);
       double t = (double)rounds * t_unit + 3e-6 + fixed;
       // split partials: written once and read once by the reduce kernel (~5 TB/s), plus the
-      // reduce launch
-      if (se > 1) t += 2.0 * (double)se * (double)M * (double)K * 4.0 / 5.0e12 + 8e-6;
+      // reduce launch and ~0.5 us per chunk (fit to split sweeps of the mid-size tiles)
+      if (se > 1) t += 2.0 * (double)se * (double)M * (double)K * 4.0 / 5.0e12 + 8e-6 + 0.5e-6 * (double)se;
       if (t < best * 0.999) {
         best = t;
         p.kernel = kernel;
@@ -202,8 +202,36 @@ GradAPlan plan_grad_a(int64_t M, int64_t N, int64_t K) {
   consider(0, 2, 256, 256, 1, 0.19, 0.0);
   consider(0, 1, 128, 256, 2, 0.24, 0.0);
   if (wide_kernel_supported(M, N, K)) {
+    const double frag_pass = 6.0 * (double)M * (double)N / 5.5e12 + 2e-6;
     consider(3, 1, wide_tile_rows(), wide_tile_cols(), 1, 0.28, 0.0);
-    consider(5, 1, wide_tile_rows(), wide_tile_cols(), 1, 0.40, 6.0 * (double)M * (double)N / 5.5e12 + 2e-6);
+    consider(5, 1, wide_tile_rows(), wide_tile_cols(), 1, 0.40, frag_pass);
+    // Mid-size tiles run two workgroups per CU, and the time follows the
+    // busiest CU's count of them: pairs at 0.376 of its MFMA rate and an odd
+    // one alone at 0.26 (fit to the sweep at 2048 x 1536 x 1536 and
+    // 4096 x 1536 x 8960, where they beat the 512 x 128 tiles by 5-6%).
+    // Unlike the other kernels they split small problems too: at
+    // 600 x 1024 x 448 four chunks ran in 16.4 us against 24.5 unsplit.
+    const int64_t tiles = cdiv(M, mid_tile_rows()) * cdiv(K, wide_tile_cols());
+    const int64_t max_split = tiles >= 2 * kCUs ? 1 : cdiv(N, 64);
+    for (int64_t s = 1; s <= std::min<int64_t>(max_split, 16); ++s) {
+      const int64_t chunk = cdiv(cdiv(N, s), 64) * 64;
+      const int64_t se = cdiv(N, chunk);
+      if (se != s) continue;
+      const int64_t units = tiles * se;
+      const int64_t load = cdiv(units, (int64_t)kCUs);
+      const double flop = (double)mid_tile_rows() * (double)wide_tile_cols() * (double)chunk * 2.0;
+      double t = (double)(load / 2) * 2.0 * flop / (cu_rate * 0.376) + (double)(load % 2) * flop / (cu_rate * 0.26) +
+                 3e-6 + frag_pass;
+      if (se > 1) t += 2.0 * (double)se * (double)M * (double)K * 4.0 / 5.0e12 + 8e-6 + 0.5e-6 * (double)se;
+      if (t < best * 0.999) {
+        best = t;
+        p.kernel = 9;
+        p.rb = 1;
+        p.splits = (int)se;
+        p.n_chunk = (int)chunk;
+        p.grid = (int)units;
+      }
+    }
   }
   return p;
 }
@@ -248,14 +276,15 @@ bool make_plan(int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, 
     p.n_chunk = (int)chunk;
     p.splits = (int)cdiv(N, chunk);
     p.grid = (int)(cdiv(K, kLinesBK) * p.splits);
-  } else if (kernel == 5 || kernel == 6) {
+  } else if (kernel == 5 || kernel == 6 || kernel == 9) {
     if (!wide_kernel_supported(M, N, K)) return false;
+    if (kernel == 9 && rb != 1 && rb != 3) return false;
     const int64_t chunk = cdiv(cdiv(N, splits), 64) * 64;
     p.kernel = kernel;
-    p.rb = 1;
+    p.rb = kernel == 9 ? rb : 1;
     p.n_chunk = (int)chunk;
     p.splits = (int)cdiv(N, chunk);
-    p.grid = (int)(cdiv(M, wide_tile_rows()) * cdiv(K, wide_tile_cols()) * p.splits);
+    p.grid = (int)(cdiv(M, kernel == 9 ? mid_tile_rows() : wide_tile_rows()) * cdiv(K, wide_tile_cols()) * p.splits);
   } else if (kernel == 3) {
     if (!wide_kernel_supported(M, N, K)) return false;
     const int64_t chunk = cdiv(cdiv(N, splits), 64) * 64;
@@ -288,7 +317,7 @@ static PlanWorkspace plan_workspace(const GradAPlan& p, int64_t M, int64_t N, in
   if (p.kernel == 2) return w;
   w.part = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)K * sizeof(float) : 0;
   w.part_al = (w.part + 255) & ~(size_t)255;
-  w.frag = (p.kernel == 5 || p.kernel == 6) ? wide_frag_bytes(M, N) : 0;
+  w.frag = (p.kernel == 5 || p.kernel == 6 || p.kernel == 9) ? wide_frag_bytes(M, N) : 0;
   w.frag_al = (w.frag + 255) & ~(size_t)255;
   w.bfrag = p.kernel == 6 ? unfused_bfrag_bytes(N, K) : 0;
   return w;
@@ -395,6 +424,9 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
   } else if (p.kernel == 6) {
     e = launch_grad_a_unfused(p.grid, grad_out, frags, bfrags, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
                               (int)cdiv(M, wide_tile_rows()), (int)cdiv(K, wide_tile_cols()), stream);
+  } else if (p.kernel == 9) {
+    e = launch_grad_a_mid_frag(p.rb, p.grid, grad_out, frags, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
+                               (int)cdiv(M, mid_tile_rows()), (int)cdiv(K, wide_tile_cols()), stream);
   } else if (p.kernel == 5) {
     e = launch_grad_a_wide_frag(p.grid, grad_out, frags, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
                                 (int)cdiv(M, wide_tile_rows()), (int)cdiv(K, wide_tile_cols()), stream);

@@ -154,9 +154,11 @@ const char* nf4_status_string(int status);
  * (0 = tiled, 1 = skinny M <= 16, 2 = zero fill for N == 0, 3 = wide tiled
  * 512 x 128 converting fp32 grad_out in its loop, 4 = streaming M <= 16 with
  * 128-column strips, 5 = wide tiled 512 x 128 fed by an fp16 A-fragment
- * conversion pass of grad_out), the kernel's tile parameter (tiled: 32-row
- * blocks per wave; wide: 1; 0 for the others), number of N-chunks (1 = no
- * split partials), rows per N-chunk, workgroups of the main launch.
+ * conversion pass of grad_out, 9 = mid-size tiles of 256 x 128 fed by the
+ * same pass, two workgroups per CU), the kernel's tile parameter (tiled:
+ * 32-row blocks per wave; wide: 1; mid-size: k-steps of A fragments in
+ * flight; 0 for the others), number of N-chunks (1 = no split partials),
+ * rows per N-chunk, workgroups of the main launch.
  * Returns NF4_ERR_SHAPE / NF4_ERR_NULL like nf4_grad_a.
  */
 int nf4_grad_a_plan(int64_t M, int64_t N, int64_t K, int* out5);
@@ -177,7 +179,10 @@ int nf4_grad_a_plan(int64_t M, int64_t N, int64_t K, int* out5);
  * N % 4 == 0 and grad_out and the codes below 2 GiB; 256-column strips of
  * whole code lines; `rb` 0..4 = rows of each lane's 4 decoded in registers
  * from byte planes, the rest by 16-bit table reads, 5 = one row through the
- * shared codebook: every `rb` gives bitwise the same result); `splits` =
+ * shared codebook: every `rb` gives bitwise the same result), kernel 9 =
+ * mid-size tiles of 256 x 128 fed by the kernel-5 fragment pass (same
+ * requirements and workspace as kernel 5; `rb` 1 or 3 = k-steps of A
+ * fragments in flight; bitwise the same result as kernel 5); `splits` =
  * requested number of N-chunks (rounded so
  * that every chunk but the last is a whole number of stages).  Same contract
  * and results-to-bound as nf4_grad_a; NF4_ERR_SHAPE if the forced plan does

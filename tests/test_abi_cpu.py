@@ -96,8 +96,8 @@ def test_plan_is_consistent(nb, M, N, K):
     if M <= 16:
         assert p["kernel"] in ("skinny", "stream")
     else:
-        assert p["kernel"] in ("tile", "wide", "wide16")
-    if p["kernel"] in ("wide", "wide16"):  # only where the wide kernel's preconditions hold
+        assert p["kernel"] in ("tile", "wide", "wide16", "mid")
+    if p["kernel"] in ("wide", "wide16", "mid"):  # only where the wide kernel's preconditions hold
         assert N % 64 == 0 and M * N * 4 < 2 ** 31 and N * K // 2 < 2 ** 31
     assert p["splits"] >= 1
     assert p["n_chunk"] * p["splits"] >= N > p["n_chunk"] * (p["splits"] - 1)
@@ -114,5 +114,5 @@ def test_plan_is_consistent(nb, M, N, K):
         assert p["grid"] == -(-M // bm) * tiles_k * p["splits"]
     else:
         assert p["n_chunk"] % 64 == 0 and p["rb"] == 1
-        bm, bk = 512, 128
+        bm, bk = (256 if p["kernel"] == "mid" else 512), 128
         assert p["grid"] == -(-M // bm) * -(-K // bk) * p["splits"]

@@ -182,6 +182,26 @@ def test_grad_a_wide16_variants_ragged(lib, splits, M, N, K):
                  what=f"wide16 s{splits} {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("rb,splits", [(1, 1), (3, 1), (1, 3), (3, 2)])
+@pytest.mark.parametrize("M,N,K", [(17, 64, 64), (255, 384, 768), (257, 640, 320), (600, 1024, 448),
+                                   (1030, 256, 1088), (31, 128, 128)])
+def test_grad_a_mid_variants_ragged(lib, rb, splits, M, N, K):
+    """Mid-size 256 x 128 tiles (four waves, two workgroups per CU) on the fp16 A fragments: ragged M around
+    the 256-row tile, ragged K, N splits, both fragment prefetch depths; within the bound and bitwise equal to
+    the 512 x 128 kernel (same operands, same reduction order)."""
+    g, s, b = random_inputs(M, N, K, seed=M + 3 * N + K + 11 * rb + 19 * splits)
+    got = check_grad_a(lib, g, s, b, M, N, K, kernel="mid", rb=rb, splits=splits,
+                       what=f"mid rb{rb} s{splits} {M}x{N}x{K}")
+    ref = host(lib.grad_a_forced(dev(g), dev(s), dev(b), "wide16", rb=1, splits=splits))
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_grad_a_mid_rejects_unsupported_depth(lib):
+    g, s, b = random_inputs(64, 128, 128, seed=3)
+    with pytest.raises(lib.Nf4Error):
+        lib.grad_a_forced(dev(g), dev(s), dev(b), "mid", rb=2)
+
+
 def test_grad_a_wide16_matches_wide_bitwise(lib):
     """Both grad_out paths give the same fp16 operands in the same reduction order, so the results are
     bitwise equal."""
@@ -515,7 +535,7 @@ _FP16_EDGE_VALUES = np.array([
     1024.5, 2049.0, 65504.0, -65504.0, 65519.0, -65519.0, 0.1, -0.3333333], dtype=np.float32)
 
 _PLANS = [(None, 1, 1), ("tile", 1, 1), ("tile", 2, 2), ("wide", 1, 1), ("wide", 2, 1), ("wide16", 1, 2),
-          ("skinny", 0, 2), ("stream", 0, 2)]
+          ("mid", 1, 2), ("skinny", 0, 2), ("stream", 0, 2)]
 
 
 @pytest.mark.parametrize("kernel,rb,splits", _PLANS, ids=lambda v: str(v))
