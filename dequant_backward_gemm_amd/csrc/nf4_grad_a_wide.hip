@@ -455,11 +455,14 @@ __device__ __forceinline__ void wide_tile(const void* __restrict__ Gv, const flo
     if constexpr (!BCOPY) prep(xc);
     // k-step s: convert grad_out of s and issue the loads of the next k-step,
     // then 8 ticks, one per MFMA tile t (4 MFMAs, one per row block).  B
-    // fragments are read three ticks ahead through a ring of four; the decode
+    // fragments are read three ticks ahead through a ring of four, across the
+    // two k-steps of the stage (the stage's buffer is complete since its
+    // barrier), so only the stage's first MFMAs wait on a fresh read; the decode
     // of columns 4s .. 4s+3 of the next stage (table reads, then two ticks
     // later the pack and fragment store) and the per-stage extras are spread
     // over the ticks.  Scheduling barriers between ticks keep every load where
     // it is issued (the compiler would otherwise sink loads to their uses).
+    u32x4 bf[4];
     for_each_index(std::make_integer_sequence<int, 2>{}, [&](auto sc_) {
       constexpr int s = decltype(sc_)::value;
       constexpr int c0 = 4 * s;  // decode columns c0 .. c0 + 3 in this k-step
@@ -483,11 +486,13 @@ __device__ __forceinline__ void wide_tile(const void* __restrict__ Gv, const flo
         __builtin_amdgcn_sched_barrier(0);
         to_a_frags(rr, af);
       }
-      auto read_b = [&](int t) { return lds_load_u32x4(smem, rbase + frd + (uint32_t)((s * WC * 8 + t) * 1024)); };
-      u32x4 bf[4];
-      bf[0] = read_b(0);
-      bf[1] = read_b(1);
-      bf[2] = read_b(2);
+      // B fragments of tick g = 8 k-step + tile of the stage
+      auto read_b = [&](int g) { return lds_load_u32x4(smem, rbase + frd + (uint32_t)(((g / 8) * WC * 8 + g % 8) * 1024)); };
+      if constexpr (s == 0) {
+        bf[0] = read_b(0);
+        bf[1] = read_b(1);
+        bf[2] = read_b(2);
+      }
       uint32_t lk[2][WC][2];
       __builtin_amdgcn_sched_barrier(0);
       for_each_index(std::make_integer_sequence<int, 8>{}, [&](auto tc) {
@@ -495,7 +500,7 @@ __device__ __forceinline__ void wide_tile(const void* __restrict__ Gv, const flo
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
           acc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(af[rb]), as_half8(bf[t % 4]), acc[rb][t], 0, 0, 0);
-        if constexpr (t + 3 < 8) bf[(t + 3) % 4] = read_b(t + 3);
+        if constexpr (8 * s + t + 3 < 16) bf[(t + 3) % 4] = read_b(8 * s + t + 3);
         if constexpr (BCOPY) {
           if constexpr (t == 2 && s == 0) store_bf(fwr, bfx);
           if constexpr (t == 6 && s == 0) load_bf(st + 2, bfn);
@@ -737,9 +742,10 @@ __device__ __forceinline__ void mid_tile(const void* __restrict__ Gv, const floa
 
   // One stage: MFMAs on fragment buffer P, decode of stage st+1 into buffer
   // P^1 with tables P^1, tables of stage st+2 into table buffer P.  Per
-  // k-step, eight ticks (one MFMA tile each, eight row blocks): B fragments
-  // read three ticks ahead through a ring of four; the decode of columns
-  // 4s .. 4s+3 of the next stage and the per-stage extras spread over them.
+  // k-step, eight ticks (one MFMA tile each, four row blocks): B fragments
+  // read three ticks ahead through a ring of four across the stage's two
+  // k-steps; the decode of columns 4s .. 4s+3 of the next stage and the
+  // per-stage extras spread over them.
   auto stage = [&](int st, auto par) {
     constexpr uint32_t P = decltype(par)::value;
     constexpr uint32_t toff_dec = (P ^ 1u) * kTabStage, toff_build = P * kTabStage;
@@ -747,24 +753,26 @@ __device__ __forceinline__ void mid_tile(const void* __restrict__ Gv, const floa
     uint32_t xn[2][2];
     float scn[2];
     prep(xc);
+    u32x4 bf[4];
     for_each_index(std::make_integer_sequence<int, 2>{}, [&](auto sc_) {
       constexpr int s = decltype(sc_)::value;
       constexpr int c0 = 4 * s;
       constexpr int b = (2 * (int)P + s) % NAB;
       load_af(2 * st + s + AF, afr[(b + AF) % NAB]);
       __builtin_amdgcn_sched_barrier(0);
-      auto read_b = [&](int t) { return lds_load_u32x4(smem, rbase + frd + (uint32_t)((s * 8 + t) * 1024)); };
-      u32x4 bf[4];
-      bf[0] = read_b(0);
-      bf[1] = read_b(1);
-      bf[2] = read_b(2);
+      auto read_b = [&](int g) { return lds_load_u32x4(smem, rbase + frd + (uint32_t)(g * 1024)); };
+      if constexpr (s == 0) {
+        bf[0] = read_b(0);
+        bf[1] = read_b(1);
+        bf[2] = read_b(2);
+      }
       uint32_t lk[2][2][2];
       __builtin_amdgcn_sched_barrier(0);
       for_each_index(std::make_integer_sequence<int, 8>{}, [&](auto tc) {
         constexpr int t = decltype(tc)::value;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) mfma_acc(acc[rb][t], afr[b][rb], bf[t % 4]);
-        if constexpr (t + 3 < 8) bf[(t + 3) % 4] = read_b(t + 3);
+        if constexpr (8 * s + t + 3 < 16) bf[(t + 3) % 4] = read_b(8 * s + t + 3);
         if constexpr (t >= 2 && t < 6) store_col(std::integral_constant<int, c0 + t - 2>{}, fwr, lk[t & 1]);
         if constexpr (t < 4) lookup_col(std::integral_constant<int, c0 + t>{}, toff_dec, lk[t & 1]);
         if constexpr (t == 6 && s == 0) load_codes(st + 2, xn);
