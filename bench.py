@@ -241,9 +241,10 @@ def copy_bandwidth(torch, trials=5):
 
 
 def time_config(torch, nb, M, N, K, seed, g_std, rotate_bytes=512 << 20, target_s=0.02, trials=5, op="grad_a",
-                splits=1):
+                splits=1, graph=False):
     """Median per-call time of nf4_grad_a (or, op="forward", nf4_forward) over rotated input sets (each set:
-    codes, scales, grad_out [M][N] or activations [M][K])."""
+    codes, scales, grad_out [M][N] or activations [M][K]): (median, min, max, input sets, per-call time of
+    the same calls replayed from a HIP graph if `graph`, else None)."""
     per_set = alg_bytes(M, N, K)
     nsets = max(2, -(-rotate_bytes // per_set))
     nsets = min(nsets, 64)
@@ -289,10 +290,44 @@ def time_config(torch, nb, M, N, K, seed, g_std, rotate_bytes=512 << 20, target_
         e1.record()
         torch.cuda.synchronize()
         res.append(e0.elapsed_time(e1) * 1e-3 / reps)
+    graph_s = graph_time(torch, call, sets) if graph else None
     del sets
     torch.cuda.empty_cache()
     res.sort()
-    return res[len(res) // 2], res[0], res[-1], nsets
+    return res[len(res) // 2], res[0], res[-1], nsets, graph_s
+
+
+def graph_time(torch, call, sets, replays=20):
+    """Per-call device time with the host's launch cost taken out: up to 32 calls over the rotated input
+    sets captured in one HIP graph (on a stream whose workspace an eager call has sized first), replayed;
+    median over `replays` replays of the elapsed time between events around a replay, per call."""
+    st = torch.cuda.Stream()
+    ncap = min(len(sets), 32) if len(sets) >= 8 else 4 * len(sets)
+    with torch.cuda.stream(st):
+        for r in range(len(sets)):
+            g, s, c, o = sets[r]
+            call(g, s, c, out=o)
+    st.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        for r in range(ncap):
+            g, s, c, o = sets[r % len(sets)]
+            call(g, s, c, out=o)
+    res = []
+    with torch.cuda.stream(st):
+        graph.replay()
+        for _ in range(replays):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            graph.replay()
+            e1.record(st)
+            e1.synchronize()
+            res.append(e0.elapsed_time(e1) * 1e-3 / ncap)
+    st.synchronize()
+    del graph
+    res.sort()
+    return res[len(res) // 2]
 
 
 def unfused_splits(M, N, K):
@@ -312,10 +347,10 @@ def per_config_unfused(torch, nb):
     out = {}
     for i, shp in enumerate(shapes):
         gstd = 1.0 if shp.M <= 16 else 1e-2
-        fused, _, _, _ = time_config(torch, nb, shp.M, shp.N, shp.K, seed=i, g_std=gstd)
+        fused, _, _, _, _ = time_config(torch, nb, shp.M, shp.N, shp.K, seed=i, g_std=gstd)
         plan = nb.grad_a_plan(shp.M, shp.N, shp.K)
         sp = plan["splits"] if plan["kernel"] in ("wide", "wide16", "mid") else unfused_splits(shp.M, shp.N, shp.K)
-        unf, _, _, nsets = time_config(torch, nb, shp.M, shp.N, shp.K, seed=i, g_std=gstd, op="unfused", splits=sp)
+        unf, _, _, nsets, _ = time_config(torch, nb, shp.M, shp.N, shp.K, seed=i, g_std=gstd, op="unfused", splits=sp)
         fl = 2.0 * shp.M * shp.N * shp.K
         out[shp.name] = {"M": shp.M, "N": shp.N, "K": shp.K, "fused_us": round(fused * 1e6, 2),
                          "unfused_us": round(unf * 1e6, 2), "unfused_over_fused": round(unf / fused, 3),
@@ -338,7 +373,8 @@ def per_config_table(torch, nb, op="grad_a"):
         plan.append(("full_step", full, 1e-2))
     for cname, shapes, gstd in plan:
         for i, shp in enumerate(shapes):
-            med, lo, hi, nsets = time_config(torch, nb, shp.M, shp.N, shp.K, seed=i, g_std=gstd, op=op)
+            med, lo, hi, nsets, graph_s = time_config(torch, nb, shp.M, shp.N, shp.K, seed=i, g_std=gstd, op=op,
+                                                      graph=True)
             fl = 2.0 * shp.M * shp.N * shp.K
             by = alg_bytes(shp.M, shp.N, shp.K)
             tf = fl / med / 1e12
@@ -352,6 +388,10 @@ def per_config_table(torch, nb, op="grad_a"):
                 "frac_of_roofline_time": round(roofline_time(shp.M, shp.N, shp.K) / med, 4),
                 "rotated_input_sets": nsets,
             }
+            if graph_s is not None:
+                # the same calls replayed from a HIP graph: device time without the host's per-call cost
+                out[shp.name]["graph_us"] = round(graph_s * 1e6, 2)
+                out[shp.name]["graph_tflops"] = round(fl / graph_s / 1e12, 2)
             if op == "grad_a":
                 out[shp.name]["plan"] = nb.grad_a_plan(shp.M, shp.N, shp.K)
             log(f"[bench] {op} {shp.name}: {med * 1e6:.1f} us  {tf:.1f} TFLOP/s  {gb:.0f} GB/s")
