@@ -77,17 +77,21 @@ __device__ __forceinline__ void stream_strip(const float* __restrict__ G, const 
   const uint32_t cvoff = 8u * q * crow + (uint32_t)(k0 / 2 + 4 * ci);
   // table reads of lane (ci, q): row e at +256e, group q, block ci / 8, code c at +2c
   const uint32_t tlook = wbase + 64u * (uint32_t)q + 32u * (uint32_t)(ci >> 3);
-  // table built by lane L: row L / 2 (= 8q + e), block L % 2
-  const int trow = lane >> 1, tkb = lane & 1;
+  // table built by lane L: row 8q + e with e = L / 8, q = (L / 2) % 4, block L % 2, so that the 32-byte
+  // tables eight consecutive lanes store sit at distinct offsets modulo 256 bytes (distinct banks)
+  const int tkb = lane & 1, trow = 8 * ((lane >> 1) & 3) + (lane >> 3);
   const uint32_t tbuild = wbase + 256u * (trow & 7) + 64u * (trow >> 3) + 32u * tkb;
   const uint32_t svoff = (uint32_t)trow * srow + 4u * (uint32_t)(k0 / 64 + tkb);
   // grad_out as loaded by lane L: row L / 4, values 8 * (L % 4) .. + 7 of the k-step;
-  // staged at the A-operand slot of lane 16 * (L % 4) + L / 4
+  // staged at the A-operand slot of lane 16 * (L % 4) + L / 4.  Slot s of the 1 KiB area sits at
+  // 16 * (s ^ 4 * (s / 16 % 4)) bytes (a permutation inside each group of 16 slots), so that 16
+  // consecutive lanes store to, and read from, 16 distinct 16-byte bank groups
   const int arow = lane >> 2, aq = lane & 3;
   // rows >= M read through an offset past the buffer's range: zero, no memory traffic
   const uint32_t avoff = (arow < M) ? (uint32_t)arow * (uint32_t)N * 4u + 32u * aq : 0x80000000u;
-  const uint32_t astore = wbase + kSkTabBytes + 16u * (uint32_t)(16 * aq + arow);
-  const uint32_t aread = wbase + kSkTabBytes + 16u * (uint32_t)lane;
+  auto aslot = [](uint32_t s) { return 16u * (s ^ (4u * ((s >> 4) & 3u))); };
+  const uint32_t astore = wbase + kSkTabBytes + aslot((uint32_t)(16 * aq + arow));
+  const uint32_t aread = wbase + kSkTabBytes + aslot((uint32_t)lane);
 
   floatx4 acc[8];
 #pragma unroll
