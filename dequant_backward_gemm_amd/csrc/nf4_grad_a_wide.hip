@@ -556,23 +556,6 @@ __device__ __forceinline__ void wide_tile(const void* __restrict__ Gv, const flo
   }
 }
 
-// acc += A . B, one 16x16x32 fp16 MFMA with the accumulator in AGPRs, as
-// inline assembly: left to itself the compiler keeps some of the mid-size
-// tile's accumulators in VGPRs and copies them between the two files around
-// the MFMAs.  The hardware does not interlock every dependency of an MFMA,
-// and the compiler inserts the required wait states only around MFMAs it
-// issued itself, so the rules that keep this safe are local: the operands
-// come from loads only (no VALU instruction writes them), an MFMA reading as
-// SrcC the exact AGPRs the previous MFMA of the same shape wrote needs no
-// wait states, and the accumulators are zeroed and read back only behind
-// explicit waits with scheduling fences (below).  tests/test_asm_hazards.py
-// scans the compiled code of every kernel that uses it for a VALU write of an
-// MFMA operand within two wait states before the MFMA and for a read of an
-// MFMA result within 19 wait states after it.
-__device__ __forceinline__ void mfma_acc(floatx4_t& acc, const u32x4& a, const u32x4& b) {
-  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
 // Mid-size tile: 256 x 128 with four waves (256 threads) and two workgroups
 // per CU, for problems whose 512 x 128 tiles leave CUs idle or end in a thin
 // last round.  Wave w owns rows 64w .. 64w + 63 (four 16-row blocks x eight
@@ -648,11 +631,6 @@ __device__ __forceinline__ void mid_tile(const void* __restrict__ Gv, const floa
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[rb][t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  // the zeroing VALU writes must be two wait states ahead of the first MFMA
-  // that reads them as its accumulator input
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 1" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
 
   auto load_codes = [&](int st, uint32_t (&x)[2][2]) {
     const uint32_t r0 = stage_row(st);
@@ -771,7 +749,8 @@ __device__ __forceinline__ void mid_tile(const void* __restrict__ Gv, const floa
       for_each_index(std::make_integer_sequence<int, 8>{}, [&](auto tc) {
         constexpr int t = decltype(tc)::value;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) mfma_acc(acc[rb][t], afr[b][rb], bf[t % 4]);
+        for (int rb = 0; rb < RB; ++rb)
+          acc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(afr[b][rb]), as_half8(bf[t % 4]), acc[rb][t], 0, 0, 0);
         if constexpr (8 * s + t + 3 < 16) bf[(t + 3) % 4] = read_b(8 * s + t + 3);
         if constexpr (t >= 2 && t < 6) store_col(std::integral_constant<int, c0 + t - 2>{}, fwr, lk[t & 1]);
         if constexpr (t < 4) lookup_col(std::integral_constant<int, c0 + t>{}, toff_dec, lk[t & 1]);
@@ -798,13 +777,6 @@ __device__ __forceinline__ void mid_tile(const void* __restrict__ Gv, const floa
   }
   if (st < nst) stage(st, std::integral_constant<uint32_t, 0>{});
 
-  // The MFMAs above are issued as inline assembly (accumulators pinned to
-  // AGPRs), which the compiler's hazard tracking does not see: wait out the
-  // last MFMAs' write-back before the accumulators are read, with scheduling
-  // fences so that no read moves above the wait.
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
   // 16x16 accumulator layout: lane (ci, q), register r -> row 4*q + r, column ci.
   const int ci = lane & 15, q = lane >> 4;
   const int col = k0 + 8 * ci;
