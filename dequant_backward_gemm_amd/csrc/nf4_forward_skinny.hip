@@ -92,14 +92,21 @@ __device__ __forceinline__ void forward_strip(const float* __restrict__ A, const
   // scale of lane (ci, q): row ci, block 2s + q / 2
   const uint32_t svoff = (uint32_t)ci * srow + 4u * (uint32_t)(q >> 1);
   // activations loaded by thread t: row t / 32, k = 128s + 4 (t % 32) .. + 3;
-  // stored as A operand u of lane (row, k / 32) at half 4 ((t % 32) & 1)
+  // stored as A operand u of lane L = 16 (k / 32) + row at half 4 ((t % 32) & 1).
+  // Operand u of lane L sits at slot L ^ (4u + L / 16) of the operand's 1 KiB
+  // (a permutation inside each group of 16 lanes), so that the 32 threads of a
+  // row store to 32 distinct 8-byte bank positions and 16 lanes read 16
+  // distinct 16-byte slots
   const int arow = tid >> 5, af4 = tid & 31;
   const bool arow_ok = arow < M;
   const uint32_t avoff = ((uint32_t)arow * (uint32_t)K + 4u * (uint32_t)af4) * 4u;
   const uint32_t abase = kFsWaves * kFsTabBytes;
+  const int au = (af4 >> 1) & 3, aq = af4 >> 3;
   const uint32_t astore =
-      abase + (uint32_t)((((af4 >> 1) & 3) * 64 + 16 * (af4 >> 3) + arow) * 16 + 8 * (af4 & 1));
-  const uint32_t aread = abase + 16u * (uint32_t)lane;
+      abase + (uint32_t)(au * 1024 + 16 * ((16 * aq + arow) ^ (4 * au + aq)) + 8 * (af4 & 1));
+  uint32_t aread[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) aread[u] = abase + (uint32_t)(u * 1024 + 16 * (lane ^ (4 * u + q)));
 
   floatx4 acc[T];
 #pragma unroll
@@ -161,7 +168,7 @@ __device__ __forceinline__ void forward_strip(const float* __restrict__ A, const
       constexpr int i = decltype(ic)::value;
       constexpr int u = i / T, t = i % T;
       if constexpr (i + 1 < 4 * T) lookup(std::integral_constant<int, i + 1>{}, lk[(i + 1) & 1]);
-      if constexpr (t == 0) af = lds_load_u32x4(smem, aread + b * kFsABytes + 1024u * u);
+      if constexpr (t == 0) af = lds_load_u32x4(smem, aread[u] + b * kFsABytes);
       u32x4 bf;
 #pragma unroll
       for (int p = 0; p < 4; ++p) bf[p] = pack_half2_rne(d.sc[t] * lk[i & 1][2 * p], d.sc[t] * lk[i & 1][2 * p + 1]);
