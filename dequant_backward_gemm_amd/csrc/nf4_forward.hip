@@ -89,13 +89,18 @@ __global__ __launch_bounds__(512, 1) void nf4_forward_kernel(const void* __restr
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
     voff_a[rb] = ((uint32_t)((m0 + 64 * wave) / 16 + rb) * (uint32_t)(K / 32) * 64u + (uint32_t)lane) * 16u;
-  const uint32_t rbase = kFwFragBase + 16u * (uint32_t)lane;
+  // B fragment slot of MFMA lane l inside its tile's 1 KiB: l ^ (4 (l / 16)), a permutation
+  // inside each group of 16 lanes (the decode stores below stay conflict-free)
+  const uint32_t rbase = kFwFragBase + 16u * (uint32_t)(lane ^ (4 * q));
 
-  // ---- decode role: slot (k-step s, tile wave, lane): row 8ci + wave of the tile ----
-  const uint32_t drow = (uint32_t)(8 * ci + wave);
-  const uint32_t cvoff = (uint32_t)(n0 + drow) * crow + 4u * (uint32_t)q;
+  // ---- decode role: slot (k-step s, tile wave, MFMA lane dc + 16 dq): row 8 dc + wave ----
+  // Decode lane L takes dc = (L / 4) % 16, dq = L % 4, so the 32 lanes of a half-wave read the
+  // tables of 8 rows (256 contiguous bytes: distinct banks) instead of 16
+  const int dc = (lane >> 2) & 15, dq = lane & 3;
+  const uint32_t drow = (uint32_t)(8 * dc + wave);
+  const uint32_t cvoff = (uint32_t)(n0 + drow) * crow + 4u * (uint32_t)dq;
   const uint32_t tb = kFwTabBase + fw_tab_pos(drow) * 32u;
-  const uint32_t wb = kFwFragBase + 16u * (uint32_t)tid;  // + s * 8 KiB
+  const uint32_t wb = kFwFragBase + (uint32_t)wave * 1024u + 16u * (uint32_t)((dc + 16 * dq) ^ (4 * dq));  // + s * 8 KiB
 
   // ---- table role: table of stage row tid / 4, levels 4 (tid % 4) .. + 3 ----
   const uint32_t trow = (uint32_t)(tid >> 2);
