@@ -762,19 +762,19 @@ def main():
     for p, a, b in events["done"]:
         N, K = shapes[p]
         name = kernel_name_for(nb.grad_a_plan(M_STEP, N, K), N)
-        d = by_kernel.setdefault(name, [0.0, 0.0, 0])
+        d = by_kernel.setdefault(name, [0.0, 0.0, 0, 0.0])
         d[0] += a.elapsed_time(b) * 1e-3
         d[1] += 2.0 * M_STEP * N * K
         d[2] += 1
+        d[3] += alg_bytes(M_STEP, N, K)
     dom = max(by_kernel, key=lambda k: by_kernel[k][0])
-    dsec, dflop, dn = by_kernel[dom]
+    dsec, dflop, dn, dbytes = by_kernel[dom]
     achieved = dflop / dsec / 1e12
     traffic = recorded_traffic()
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": traffic,
             "kernel": dom, "launches": dn, "avg_launch_us": round(dsec / dn * 1e6, 1),
-            "flop_per_launch": round(dflop / dn), "alg_bytes_per_launch":
-                round(sum(alg_bytes(M_STEP, N, K) for (_, N, K) in PROJ) / len(PROJ)),
+            "flop_per_launch": round(dflop / dn), "alg_bytes_per_launch": round(dbytes / dn),
             "share_of_step_time": round(dsec / (ms_total * 1e-3), 4),
             "kernel_source_digest": source_digest()}
 
