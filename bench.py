@@ -121,6 +121,8 @@ def kernel_name_for(plan, N=None):
         return "grad_out_frag_kernel<false>+grad_a_wide_kernel<1, 3, false>"
     if plan["kernel"] == "mid":
         return "grad_out_frag_kernel<false>+grad_a_mid_kernel<%d>" % plan["rb"]
+    if plan["kernel"] == "small":
+        return "grad_out_frag_kernel<false>+grad_a_small_kernel"
     if plan["kernel"] == "stream":
         return "grad_a_stream_kernel<true>" if N is not None and N % 4 == 0 else "grad_a_stream_kernel<false>"
     return "grad_a_tile_kernel<%d>" % plan["rb"]
@@ -331,8 +333,9 @@ def graph_time(torch, call, sets, replays=20):
 
 
 def unfused_splits(M, N, K):
-    """N-chunk count for the unfused comparison path: the fused plan's for the large-M tile plans; for a
-    skinny M, enough chunks to give every CU a 512 x 128 tile (the path has no skinny kernel)."""
+    """N-chunk count for the unfused comparison path: the fused plan's for the 512 x 128 and 256 x 128 tile
+    plans; otherwise (skinny M, small tiles) enough chunks to give every CU a 512 x 128 tile (the path has
+    no skinny or small-tile kernel)."""
     tiles = -(-M // 512) * -(-K // 128)
     return max(1, min(N // 64, 256 // tiles)) if tiles < 256 else 1
 
@@ -349,7 +352,8 @@ def per_config_unfused(torch, nb):
         gstd = 1.0 if shp.M <= 16 else 1e-2
         fused, _, _, _, _ = time_config(torch, nb, shp.M, shp.N, shp.K, seed=i, g_std=gstd)
         plan = nb.grad_a_plan(shp.M, shp.N, shp.K)
-        sp = plan["splits"] if plan["kernel"] in ("wide", "wide16", "mid") else unfused_splits(shp.M, shp.N, shp.K)
+        fused_kernels = ("wide", "wide16", "mid")  # unsplit small tiles: the unfused path needs its own split
+        sp = plan["splits"] if plan["kernel"] in fused_kernels else unfused_splits(shp.M, shp.N, shp.K)
         unf, _, _, nsets, _ = time_config(torch, nb, shp.M, shp.N, shp.K, seed=i, g_std=gstd, op="unfused", splits=sp)
         fl = 2.0 * shp.M * shp.N * shp.K
         out[shp.name] = {"M": shp.M, "N": shp.N, "K": shp.K, "fused_us": round(fused * 1e6, 2),

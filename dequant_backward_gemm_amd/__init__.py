@@ -213,8 +213,8 @@ def grad_a_grouped(problems, outs=None, stream=None):
 def grad_a_forced(grad_out, scales, codes, kernel: str, rb: int = 2, splits: int = 1, out=None, stream=None):
     """grad_a with a forced launch plan (kernel "tile", "skinny", "wide", "stream", "wide16", "unfused": the
     comparison path with a separate fp16 dequant pass, "lines": line streaming with `rb` of each lane's 4
-    rows decoded in registers, or "mid": 256 x 128 tiles with `rb` k-steps of A fragments in flight); for
-    tests and tuning."""
+    rows decoded in registers, "mid": 256 x 128 tiles with `rb` k-steps of A fragments in flight, or
+    "small": 128 x 128 tiles, `rb` 1); for tests and tuning."""
     import torch
     M, N = grad_out.shape
     K = codes.shape[1] * 2
@@ -224,7 +224,8 @@ def grad_a_forced(grad_out, scales, codes, kernel: str, rb: int = 2, splits: int
     if out is None:
         out = torch.empty((M, K), dtype=torch.float32, device=grad_out.device)
     _require(out, torch.float32, (M, K), "out")
-    kid = {"tile": 0, "skinny": 1, "wide": 3, "stream": 4, "wide16": 5, "unfused": 6, "lines": 8, "mid": 9}[kernel]
+    kid = {"tile": 0, "skinny": 1, "wide": 3, "stream": 4, "wide16": 5, "unfused": 6, "lines": 8, "mid": 9,
+           "small": 10}[kernel]
     _check(_lib.nf4_grad_a_forced(_ptr(grad_out), _ptr(scales), _ptr(codes), _ptr(out), M, N, K, kid, rb, splits,
                                   _stream_handle(stream)), "nf4_grad_a_forced")
     return out
@@ -345,5 +346,5 @@ def grad_a_plan(M: int, N: int, K: int) -> dict:
     out = (ctypes.c_int * 5)()
     _check(_lib.nf4_grad_a_plan(M, N, K, out), "nf4_grad_a_plan")
     kernel = {0: "tile", 1: "skinny", 2: "zero_fill", 3: "wide", 4: "stream", 5: "wide16", 6: "unfused",
-              8: "lines", 9: "mid"}[out[0]]
+              8: "lines", 9: "mid", 10: "small"}[out[0]]
     return {"kernel": kernel, "rb": out[1], "splits": out[2], "n_chunk": out[3], "grid": out[4]}

@@ -556,25 +556,28 @@ __device__ __forceinline__ void wide_tile(const void* __restrict__ Gv, const flo
   }
 }
 
-// Mid-size tile: 256 x 128 with four waves (256 threads) and two workgroups
-// per CU, for problems whose 512 x 128 tiles leave CUs idle or end in a thin
-// last round.  Wave w owns rows 64w .. 64w + 63 (four 16-row blocks x eight
-// MFMA tiles, 128 accumulators per lane, as in the eight-wave kernel), fed by
-// the same fp16 A fragments.  The decode and table roles and every LDS layout
-// are those of the eight-wave kernel, each lane playing two of its lanes
-// (waves w and w + 4), so the B operands and the reduction order are the same
-// and the results are bitwise equal to the 512 x 128 kernel's.
-template <int AF>
+// Mid-size tiles: 64 RB x 128 with four waves (256 threads), for problems
+// whose 512 x 128 tiles leave CUs idle or end in a thin last round.  RB = 4:
+// 256 x 128, wave w owns rows 64w .. 64w + 63 (four 16-row blocks x eight
+// MFMA tiles, 128 accumulators per lane, as in the eight-wave kernel), two
+// workgroups per CU.  RB = 2: 128 x 128, 32 rows per wave, three workgroups
+// per CU, for problems small enough that one round of these tiles covers
+// them without splitting N.  Both are fed by the same fp16 A fragments.  The
+// decode and table roles and every LDS layout are those of the eight-wave
+// kernel, each lane playing two of its lanes (waves w and w + 4), so the B
+// operands and the reduction order are the same and the results are bitwise
+// equal to the 512 x 128 kernel's.
+template <int AF, int RB>
 __device__ __forceinline__ void mid_tile(const void* __restrict__ Gv, const float* __restrict__ S,
                                          const uint32_t* __restrict__ C32, int M, int N, int K, int tiles_k, int tile,
                                          int nb, int ne, float* __restrict__ dst, int ld) {
   // buffer (2 P + s) % (AF + 1) must hold k-step 2 st + s for either stage parity P = st % 2
   static_assert(AF == 1 || AF == 3, "fragment prefetch depth 1 or 3");
+  static_assert(RB == 2 || RB == 4, "16-row blocks per wave: 2 or 4");
   using Cfg = WideCfg<1>;
   constexpr int BK = Cfg::BK, KB = Cfg::KB;
   constexpr uint32_t kTabStage = Cfg::kTabStage, kFragStage = Cfg::kFragStage;
-  constexpr int RB = 4;        // 16-row blocks per wave
-  constexpr int BM = 64 * RB;  // tile rows: four waves
+  constexpr int BM = 64 * RB;  // tile rows: four waves of 16 RB rows
   __shared__ __attribute__((aligned(16))) uint32_t smem[Cfg::kLds / 4];
 
   const int tid = threadIdx.x;
@@ -807,8 +810,22 @@ __global__ __launch_bounds__(256, 2) void grad_a_mid_kernel(const void* __restri
   const int tiles = tiles_m * tiles_k;
   const int split = logical / tiles;
   const int nb = split * n_chunk;
-  mid_tile<AF>(frags, S, C32, M, N, K, tiles_k, logical % tiles, nb, min(N, nb + n_chunk),
-               out + (size_t)split * (size_t)M * (size_t)K, K);
+  mid_tile<AF, 4>(frags, S, C32, M, N, K, tiles_k, logical % tiles, nb, min(N, nb + n_chunk),
+                  out + (size_t)split * (size_t)M * (size_t)K, K);
+}
+
+// 128 x 128 tiles (two 16-row blocks per wave), three workgroups per CU.
+__global__ __launch_bounds__(256, 3) void grad_a_small_kernel(const void* __restrict__ frags,
+                                                              const float* __restrict__ S,
+                                                              const uint32_t* __restrict__ C32,
+                                                              float* __restrict__ out, int M, int N, int K,
+                                                              int n_chunk, int tiles_m, int tiles_k) {
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int tiles = tiles_m * tiles_k;
+  const int split = logical / tiles;
+  const int nb = split * n_chunk;
+  mid_tile<1, 2>(frags, S, C32, M, N, K, tiles_k, logical % tiles, nb, min(N, nb + n_chunk),
+                 out + (size_t)split * (size_t)M * (size_t)K, K);
 }
 
 // One tile over one N-chunk per workgroup; the chunk index is the slowest
@@ -910,12 +927,16 @@ hipError_t launch_frag_pass(const float* src, void* frags, int rows, int cols, b
   return hipGetLastError();
 }
 
-hipError_t launch_grad_a_mid_frag(int af, int grid, const float* grad_out, void* frags, const float* scales,
-                                  const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,
-                                  int tiles_k, hipStream_t stream) {
+hipError_t launch_grad_a_mid_frag(int af, int rows, int grid, const float* grad_out, void* frags,
+                                  const float* scales, const uint32_t* codes, float* dst, int M, int N, int K,
+                                  int n_chunk, int tiles_m, int tiles_k, hipStream_t stream) {
+  if (rows != 256 && !(rows == 128 && af == 1)) return hipErrorInvalidValue;
   hipError_t e = launch_frag_pass(grad_out, frags, M, N, /*natural=*/false, stream);
   if (e != hipSuccess) return e;
-  if (af == 1)
+  if (rows == 128)
+    hipLaunchKernelGGL(grad_a_small_kernel, dim3(grid), dim3(256), 0, stream, frags, scales, codes, dst, M, N, K,
+                       n_chunk, tiles_m, tiles_k);
+  else if (af == 1)
     hipLaunchKernelGGL(grad_a_mid_kernel<1>, dim3(grid), dim3(256), 0, stream, frags, scales, codes, dst, M, N, K,
                        n_chunk, tiles_m, tiles_k);
   else

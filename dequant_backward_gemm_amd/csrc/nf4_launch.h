@@ -27,9 +27,10 @@ struct GradAPlan {
                  // 5 = wide fed by fp16 A fragments from a conversion pass (tile 512 x 128),
                  // 6 = unfused comparison path (fp16 weight pass, then a fragment-copy GEMM),
                  // 8 = line streaming (M <= 16, 256-column strips),
-                 // 9 = mid-size tiles (256 x 128, four waves, two workgroups per CU) fed by kernel 5's pass
+                 // 9 = mid-size tiles (256 x 128, four waves, two workgroups per CU) fed by kernel 5's pass,
+                 // 10 = small tiles (128 x 128, four waves, three workgroups per CU) fed by the same pass
   int rb;        // tile: 32-row blocks per wave; wide: 1; line streaming: rows decoded in registers;
-                 // mid-size: k-steps of A fragments in flight
+                 // mid-size and small: k-steps of A fragments in flight
   int splits;    // number of N-chunks (1 = no workspace, no reduce launch)
   int n_chunk;   // rows of N per chunk
   int grid;      // workgroups of the main kernel
@@ -89,13 +90,14 @@ hipError_t launch_grad_a_wide(int grid, const float* grad_out, const float* scal
 // workspace of wide_frag_bytes(M, N) bytes, then the wide kernel (tile 512 x
 // 128) reads them.  Same preconditions as the wide kernel.
 size_t wide_frag_bytes(int64_t M, int64_t N);
-// Mid-size tiles of 256 x 128 from the same fragments (four waves, two
-// workgroups per CU; bitwise the same results), `af` (1 or 3) k-steps of A
-// fragments in flight.  Tile rows: mid_tile_rows().
+// Mid-size tiles from the same fragments (four waves; bitwise the same
+// results): `rows` = 256 (two workgroups per CU, `af` 1 or 3 k-steps of A
+// fragments in flight) or 128 (three per CU, af 1), x 128 columns.
 inline int mid_tile_rows() { return 256; }
-hipError_t launch_grad_a_mid_frag(int af, int grid, const float* grad_out, void* frags, const float* scales,
-                                  const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,
-                                  int tiles_k, hipStream_t stream);
+inline int small_tile_rows() { return 128; }
+hipError_t launch_grad_a_mid_frag(int af, int rows, int grid, const float* grad_out, void* frags,
+                                  const float* scales, const uint32_t* codes, float* dst, int M, int N, int K,
+                                  int n_chunk, int tiles_m, int tiles_k, hipStream_t stream);
 hipError_t launch_grad_a_wide_frag(int grid, const float* grad_out, void* frags, const float* scales,
                                    const uint32_t* codes, float* dst, int M, int N, int K, int n_chunk, int tiles_m,
                                    int tiles_k, hipStream_t stream);

@@ -237,6 +237,21 @@ GradAPlan plan_grad_a(int64_t M, int64_t N, int64_t K) {
         p.grid = (int)units;
       }
     }
+    // 128 x 128 tiles, unsplit, where the plan above splits N only to fill
+    // the CUs and one round of the small tiles fills them instead: short
+    // reductions (N <= 1536) with 64..256 such tiles.  The split's partials
+    // and reduce launch cost more there than the small tiles' lower MFMA
+    // efficiency (measured: 2048 x 1536 x 1536 34.0 against 35.8 us in two
+    // chunks, 1024 x 1536 x 1536 27.4 against 31.3, 1100 x 1024 x 1088 20.1
+    // against 25.3; at N = 3584 or 4096 the split plans stay ahead by 2-45%).
+    const int64_t small = cdiv(M, small_tile_rows()) * cdiv(K, wide_tile_cols());
+    if (!tiny && p.splits > 1 && N <= 1536 && small >= 64 && small <= kCUs) {
+      p.kernel = 10;
+      p.rb = 1;
+      p.splits = 1;
+      p.n_chunk = (int)N;
+      p.grid = (int)small;
+    }
   }
   return p;
 }
@@ -281,15 +296,17 @@ bool make_plan(int64_t M, int64_t N, int64_t K, int kernel, int rb, int splits, 
     p.n_chunk = (int)chunk;
     p.splits = (int)cdiv(N, chunk);
     p.grid = (int)(cdiv(K, kLinesBK) * p.splits);
-  } else if (kernel == 5 || kernel == 6 || kernel == 9) {
+  } else if (kernel == 5 || kernel == 6 || kernel == 9 || kernel == 10) {
     if (!wide_kernel_supported(M, N, K)) return false;
     if (kernel == 9 && rb != 1 && rb != 3) return false;
+    if (kernel == 10 && rb != 1) return false;
     const int64_t chunk = cdiv(cdiv(N, splits), 64) * 64;
+    const int64_t rows = kernel == 9 ? mid_tile_rows() : kernel == 10 ? small_tile_rows() : wide_tile_rows();
     p.kernel = kernel;
     p.rb = kernel == 9 ? rb : 1;
     p.n_chunk = (int)chunk;
     p.splits = (int)cdiv(N, chunk);
-    p.grid = (int)(cdiv(M, kernel == 9 ? mid_tile_rows() : wide_tile_rows()) * cdiv(K, wide_tile_cols()) * p.splits);
+    p.grid = (int)(cdiv(M, rows) * cdiv(K, wide_tile_cols()) * p.splits);
   } else if (kernel == 3) {
     if (!wide_kernel_supported(M, N, K)) return false;
     const int64_t chunk = cdiv(cdiv(N, splits), 64) * 64;
@@ -322,7 +339,7 @@ static PlanWorkspace plan_workspace(const GradAPlan& p, int64_t M, int64_t N, in
   if (p.kernel == 2) return w;
   w.part = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)K * sizeof(float) : 0;
   w.part_al = (w.part + 255) & ~(size_t)255;
-  w.frag = (p.kernel == 5 || p.kernel == 6 || p.kernel == 9) ? wide_frag_bytes(M, N) : 0;
+  w.frag = (p.kernel == 5 || p.kernel == 6 || p.kernel == 9 || p.kernel == 10) ? wide_frag_bytes(M, N) : 0;
   w.frag_al = (w.frag + 255) & ~(size_t)255;
   w.bfrag = p.kernel == 6 ? unfused_bfrag_bytes(N, K) : 0;
   return w;
@@ -429,9 +446,10 @@ hipError_t launch_grad_a_plan(const GradAPlan& p, const float* grad_out, const f
   } else if (p.kernel == 6) {
     e = launch_grad_a_unfused(p.grid, grad_out, frags, bfrags, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
                               (int)cdiv(M, wide_tile_rows()), (int)cdiv(K, wide_tile_cols()), stream);
-  } else if (p.kernel == 9) {
-    e = launch_grad_a_mid_frag(p.rb, p.grid, grad_out, frags, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
-                               (int)cdiv(M, mid_tile_rows()), (int)cdiv(K, wide_tile_cols()), stream);
+  } else if (p.kernel == 9 || p.kernel == 10) {
+    const int rows = p.kernel == 9 ? mid_tile_rows() : small_tile_rows();
+    e = launch_grad_a_mid_frag(p.rb, rows, p.grid, grad_out, frags, scales, c32, dst, (int)M, (int)N, (int)K,
+                               p.n_chunk, (int)cdiv(M, rows), (int)cdiv(K, wide_tile_cols()), stream);
   } else if (p.kernel == 5) {
     e = launch_grad_a_wide_frag(p.grid, grad_out, frags, scales, c32, dst, (int)M, (int)N, (int)K, p.n_chunk,
                                 (int)cdiv(M, wide_tile_rows()), (int)cdiv(K, wide_tile_cols()), stream);

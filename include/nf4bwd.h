@@ -155,9 +155,10 @@ const char* nf4_status_string(int status);
  * 512 x 128 converting fp32 grad_out in its loop, 4 = streaming M <= 16 with
  * 128-column strips, 5 = wide tiled 512 x 128 fed by an fp16 A-fragment
  * conversion pass of grad_out, 9 = mid-size tiles of 256 x 128 fed by the
- * same pass, two workgroups per CU), the kernel's tile parameter (tiled:
- * 32-row blocks per wave; wide: 1; mid-size: k-steps of A fragments in
- * flight; 0 for the others), number of N-chunks (1 = no split partials),
+ * same pass, two workgroups per CU, 10 = small tiles of 128 x 128 fed by the
+ * same pass, three workgroups per CU), the kernel's tile parameter (tiled:
+ * 32-row blocks per wave; wide: 1; mid-size and small: k-steps of A
+ * fragments in flight; 0 for the others), number of N-chunks (1 = no split partials),
  * rows per N-chunk, workgroups of the main launch.
  * Returns NF4_ERR_SHAPE / NF4_ERR_NULL like nf4_grad_a.
  */
@@ -182,7 +183,8 @@ int nf4_grad_a_plan(int64_t M, int64_t N, int64_t K, int* out5);
  * shared codebook: every `rb` gives bitwise the same result), kernel 9 =
  * mid-size tiles of 256 x 128 fed by the kernel-5 fragment pass (same
  * requirements and workspace as kernel 5; `rb` 1 or 3 = k-steps of A
- * fragments in flight; bitwise the same result as kernel 5); `splits` =
+ * fragments in flight; bitwise the same result as kernel 5), kernel 10 =
+ * small tiles of 128 x 128 (as kernel 9 with `rb` 1 only); `splits` =
  * requested number of N-chunks (rounded so
  * that every chunk but the last is a whole number of stages).  Same contract
  * and results-to-bound as nf4_grad_a; NF4_ERR_SHAPE if the forced plan does

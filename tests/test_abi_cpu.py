@@ -86,6 +86,7 @@ def test_validation_runs_before_any_device_work(nb):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 18944, 3584), (16, 3584, 18944), (64, 256, 256), (2048, 1536, 1536),
+                                   (1100, 1024, 1088), (1024, 1536, 1536),
                                    (4096, 8960, 1536), (4096, 1536, 8960), (8192, 512, 3584), (8192, 18944, 3584),
                                    (8192, 3584, 18944), (17, 100, 192), (3, 0, 64)])
 def test_plan_is_consistent(nb, M, N, K):
@@ -96,8 +97,8 @@ def test_plan_is_consistent(nb, M, N, K):
     if M <= 16:
         assert p["kernel"] in ("skinny", "stream")
     else:
-        assert p["kernel"] in ("tile", "wide", "wide16", "mid")
-    if p["kernel"] in ("wide", "wide16", "mid"):  # only where the wide kernel's preconditions hold
+        assert p["kernel"] in ("tile", "wide", "wide16", "mid", "small")
+    if p["kernel"] in ("wide", "wide16", "mid", "small"):  # only where the wide kernel's preconditions hold
         assert N % 64 == 0 and M * N * 4 < 2 ** 31 and N * K // 2 < 2 ** 31
     assert p["splits"] >= 1
     assert p["n_chunk"] * p["splits"] >= N > p["n_chunk"] * (p["splits"] - 1)
@@ -114,5 +115,5 @@ def test_plan_is_consistent(nb, M, N, K):
         assert p["grid"] == -(-M // bm) * tiles_k * p["splits"]
     else:
         assert p["n_chunk"] % 64 == 0 and p["rb"] == 1
-        bm, bk = (256 if p["kernel"] == "mid" else 512), 128
+        bm, bk = {"mid": 256, "small": 128}.get(p["kernel"], 512), 128
         assert p["grid"] == -(-M // bm) * -(-K // bk) * p["splits"]

@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-KERNELS = {"tile": 0, "skinny": 1, "wide": 3, "stream": 4, "wide16": 5, "unfused": 6, "mid": 9}
+KERNELS = {"tile": 0, "skinny": 1, "wide": 3, "stream": 4, "wide16": 5, "unfused": 6, "mid": 9, "small": 10}
 
 
 @pytest.fixture(scope="module")
@@ -56,6 +56,7 @@ CASES = [
     ("wide16", 1, 1, 1030, 2048, 384), ("wide16", 1, 2, 513, 640, 320), ("wide16", 1, 1, 31, 128, 128),
     ("unfused", 1, 2, 600, 1024, 448),
     ("mid", 1, 1, 600, 1024, 448), ("mid", 3, 2, 513, 640, 320), ("mid", 1, 3, 1030, 256, 1088),
+    ("small", 1, 1, 600, 1024, 448), ("small", 1, 2, 129, 640, 320),
 ]
 
 

@@ -200,6 +200,33 @@ def test_grad_a_mid_rejects_unsupported_depth(lib):
     g, s, b = random_inputs(64, 128, 128, seed=3)
     with pytest.raises(lib.Nf4Error):
         lib.grad_a_forced(dev(g), dev(s), dev(b), "mid", rb=2)
+    with pytest.raises(lib.Nf4Error):
+        lib.grad_a_forced(dev(g), dev(s), dev(b), "small", rb=3)
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+@pytest.mark.parametrize("M,N,K", [(17, 64, 64), (127, 384, 768), (129, 640, 320), (600, 1024, 448),
+                                   (1030, 256, 1088), (31, 128, 128), (1100, 1024, 1088)])
+def test_grad_a_small_tiles_ragged(lib, splits, M, N, K):
+    """Small 128 x 128 tiles (four waves of 32 rows, three workgroups per CU) on the fp16 A fragments: ragged M
+    around the 128-row tile, ragged K, N splits; within the bound and bitwise equal to the 512 x 128 kernel
+    (same operands, same reduction order)."""
+    g, s, b = random_inputs(M, N, K, seed=M + 5 * N + K + 23 * splits)
+    got = check_grad_a(lib, g, s, b, M, N, K, kernel="small", rb=1, splits=splits,
+                       what=f"small s{splits} {M}x{N}x{K}")
+    ref = host(lib.grad_a_forced(dev(g), dev(s), dev(b), "wide16", rb=1, splits=splits))
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_grad_a_small_tiles_chosen_for_short_reductions(lib):
+    """The plan of a short reduction that the larger tiles would split (1100 x 1024 x 1088) is the unsplit
+    small-tile kernel, and the default call gives its result."""
+    M, N, K = 1100, 1024, 1088
+    assert lib.grad_a_plan(M, N, K)["kernel"] == "small"
+    g, s, b = random_inputs(M, N, K, seed=41)
+    got = check_grad_a(lib, g, s, b, M, N, K, what=f"default {M}x{N}x{K}")
+    ref = host(lib.grad_a_forced(dev(g), dev(s), dev(b), "small", rb=1, splits=1))
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
 def test_grad_a_wide16_matches_wide_bitwise(lib):
