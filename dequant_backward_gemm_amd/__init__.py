@@ -231,14 +231,15 @@ def grad_a_forced(grad_out, scales, codes, kernel: str, rb: int = 2, splits: int
     return out
 
 
-FORWARD_KERNELS = {"tile": 0, "stream": 1}
+FORWARD_KERNELS = {"tile": 0, "stream": 1, "mid": 2, "small": 3}
 
 
 def forward(a, scales, codes, out=None, stream=None, splits: int = 0, kernel: str = "auto"):
     """c[M, N] = a[M, K] . dequant(codes, scales)[N, K]^T (fp32).
 
-    splits > 0 forces the K chunk count; kernel "tile" or "stream" forces the kernel ("auto" with a forced
-    split count takes the one nf4_forward would: streaming for M <= 16, tiles otherwise)."""
+    splits > 0 forces the K chunk count; kernel "tile" (512 x 128 tiles), "mid" (256 x 128), "small"
+    (128 x 128) or "stream" forces the kernel ("auto" with a forced split count takes streaming for
+    M <= 16, 512 x 128 tiles otherwise)."""
     import torch
     M, K = a.shape
     N = codes.shape[0]

@@ -114,7 +114,7 @@ int nf4_forward(const float* a, const float* scales, const uint8_t* codes, float
 
 int nf4_forward_forced(const float* a, const float* scales, const uint8_t* codes, float* c, int64_t M, int64_t N,
                        int64_t K, int kernel, int splits, hipStream_t stream) {
-  if (splits < 1 || (kernel != nf4::kForwardTile && kernel != nf4::kForwardStream)) return NF4_ERR_SHAPE;
+  if (splits < 1 || kernel < nf4::kForwardTile || kernel > nf4::kForwardSmall) return NF4_ERR_SHAPE;
   return forward_checked(a, scales, codes, c, M, N, K, kernel, splits, stream);
 }
 

@@ -143,13 +143,19 @@ hipError_t launch_grad_a_unfused(int grid, const float* grad_out, void* afrags, 
 // reduction order, or natural order for the forward kernel.
 hipError_t launch_frag_pass(const float* src, void* frags, int rows, int cols, bool natural, hipStream_t stream);
 
-// Forward product C[M][N] = A[M][K] . dequant(W)^T (nf4_forward.hip): 512 x 128
-// tiles, K split into chunks of whole 64-wide stages; A converted first into
-// fragments (forward_frag_bytes(M, K) bytes of workspace).
+// kernel: -1 picks (streaming for M <= 16 where supported, else a tile kernel), 0 tiles of 512 x 128,
+// 1 streaming, 2 tiles of 256 x 128 (two workgroups per CU), 3 tiles of 128 x 128 (three per CU).
+constexpr int kForwardAuto = -1, kForwardTile = 0, kForwardStream = 1, kForwardMid = 2, kForwardSmall = 3;
+// Forward product C[M][N] = A[M][K] . dequant(W)^T (nf4_forward.hip): tiles of
+// forward_tile_rows(kernel) x 128 (kernel 0, 2 or 3; bitwise the same
+// results), K split into chunks of whole 64-wide stages; A converted first
+// into fragments (forward_frag_bytes(M, K) bytes of workspace).
 bool forward_supported(int64_t M, int64_t N, int64_t K);
 size_t forward_frag_bytes(int64_t M, int64_t K);
-hipError_t launch_forward(int grid, const float* a, void* frags, const float* scales, const uint32_t* codes,
-                          float* dst, int M, int N, int K, int k_chunk, int tiles_m, int tiles_n, hipStream_t stream);
+int forward_tile_rows(int kernel);
+hipError_t launch_forward(int kernel, int grid, const float* a, void* frags, const float* scales,
+                          const uint32_t* codes, float* dst, int M, int N, int K, int k_chunk, int tiles_m,
+                          int tiles_n, hipStream_t stream);
 // Streaming forward kernel for M <= 16 (nf4_forward_skinny.hip): 128-column
 // strips (16 per wave) x K chunks of whole 128-wide steps.
 bool forward_stream_supported(int64_t M, int64_t N, int64_t K);
@@ -161,9 +167,7 @@ int forward_stream_strips(int64_t N);
 hipError_t launch_forward_stream(int grid, const float* a, const float* scales, const uint32_t* codes, float* dst,
                                  float* c, uint32_t* counters, int M, int N, int K, int k_chunk, int strips,
                                  int splits, hipStream_t stream);
-// kernel: -1 picks (streaming for M <= 16 where supported, else tiles), 0 tiles, 1 streaming;
 // splits <= 0 picks the K chunk count.
-constexpr int kForwardAuto = -1, kForwardTile = 0, kForwardStream = 1;
 hipError_t launch_nf4_forward(const float* a, const float* scales, const uint8_t* codes, float* c, int64_t M,
                               int64_t N, int64_t K, int kernel, int splits, hipStream_t stream);
 

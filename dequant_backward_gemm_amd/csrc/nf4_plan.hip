@@ -536,41 +536,82 @@ static hipError_t launch_nf4_forward_stream(const float* a, const float* scales,
   return e;
 }
 
+// Tile kernel and K split of a forward product (M > 16): the same cost model
+// as the backward tiles -- one eight-wave 512 x 128 workgroup per CU at ~0.40
+// of its MFMA rate plus ~4 us per round; 256 x 128 workgroups two per CU
+// (pairs at 0.376, a lone one at 0.26) plus ~1 us per pair; split partials
+// written and read once plus the reduce launch -- and 128 x 128 tiles,
+// unsplit, where that plan splits K only to fill the CUs, the reduction is
+// short (K <= 1536) and 64..256 small tiles fill them.  Sweeps of the three
+// kernels over 1..6 chunks on eight shapes (rotated inputs): the model's
+// choice is the fastest plan or within 2% of it on seven, and on the eighth
+// (600 x 1024 x 448) 14.1 against 11.8 us for the small tiles; against the
+// 512 x 128 tiles alone it gains 15% at 2048 x 1536 x 1536 (32.7 against
+// 38.7 us), 6% at 4096 x 8960 x 1536 and 8% at 8192 x 512 x 3584.
+static void forward_tile_plan(int64_t M, int64_t N, int64_t K, int* kernel_out, int64_t* se_out, int64_t* chunk_out) {
+  const double cu_rate = 4096.0 * 2.4e9;  // fp16 MFMA flop/s per CU
+  double best = 1e30;
+  auto split_cost = [&](int64_t e) {
+    return e > 1 ? 2.0 * (double)e * (double)M * (double)N * 4.0 / 5.0e12 + 8e-6 + 0.5e-6 * (double)e : 0.0;
+  };
+  auto take = [&](double t, int kernel, int64_t e, int64_t ch) {
+    if (t < best * 0.999) {
+      best = t;
+      *kernel_out = kernel;
+      *se_out = e;
+      *chunk_out = ch;
+    }
+  };
+  const int64_t tiles = cdiv(M, forward_tile_rows(kForwardTile)) * cdiv(N, 128);
+  for (int64_t s = 1; s <= (tiles < kCUs ? 16 : 1); ++s) {
+    const int64_t ch = cdiv(cdiv(K, s), 64) * 64;
+    const int64_t e = cdiv(K, ch);
+    if (e != s) continue;
+    const int64_t rounds = cdiv(tiles * e, kCUs);
+    take((double)rounds * (512.0 * 128.0 * (double)ch * 2.0 / (cu_rate * 0.40) + 4e-6) + split_cost(e), kForwardTile,
+         e, ch);
+  }
+  const int64_t mid = cdiv(M, forward_tile_rows(kForwardMid)) * cdiv(N, 128);
+  for (int64_t s = 1; s <= (mid < 2 * kCUs ? 16 : 1); ++s) {
+    const int64_t ch = cdiv(cdiv(K, s), 64) * 64;
+    const int64_t e = cdiv(K, ch);
+    if (e != s) continue;
+    const int64_t load = cdiv(mid * e, kCUs);
+    const double flop = 256.0 * 128.0 * (double)ch * 2.0;
+    take((double)(load / 2) * 2.0 * flop / (cu_rate * 0.376) + (double)(load % 2) * flop / (cu_rate * 0.26) +
+             (double)cdiv(load, 2) * 1e-6 + split_cost(e),
+         kForwardMid, e, ch);
+  }
+  const int64_t small = cdiv(M, forward_tile_rows(kForwardSmall)) * cdiv(N, 128);
+  if (*se_out > 1 && K <= 1536 && small >= 64 && small <= kCUs) {
+    *kernel_out = kForwardSmall;
+    *se_out = 1;
+    *chunk_out = K;
+  }
+}
+
 hipError_t launch_nf4_forward(const float* a, const float* scales, const uint8_t* codes, float* c, int64_t M,
                               int64_t N, int64_t K, int kernel, int splits, hipStream_t stream) {
   if (K == 0) return launch_fill_zero((int)std::min<int64_t>(cdiv(M * N / 4, 256), 4096), c, M * N / 4, stream);
   if (kernel == kForwardStream || (kernel == kForwardAuto && forward_stream_supported(M, N, K)))
     return launch_nf4_forward_stream(a, scales, codes, c, M, N, K, splits, stream);
-  const int64_t tiles_m = cdiv(M, 512), tiles_n = cdiv(N, 128);
-  const int64_t tiles = tiles_m * tiles_n;
+  int fk = kernel == kForwardAuto ? kForwardTile : kernel;
   int64_t se = 1, chunk = K;
   if (splits > 0) {
     chunk = cdiv(cdiv(K, splits), 64) * 64;
     se = cdiv(K, chunk);
-  } else if (tiles < kCUs) {
-    const double cu_rate = 4096.0 * 2.4e9 * 0.40;  // fp16 MFMA flop/s per CU at the measured efficiency
-    double best = 1e30;
-    for (int64_t s = 1; s <= 16; ++s) {
-      const int64_t ch = cdiv(cdiv(K, s), 64) * 64;
-      const int64_t e = cdiv(K, ch);
-      if (e != s) continue;
-      const int64_t rounds = cdiv(tiles * e, kCUs);
-      double t = (double)rounds * (512.0 * 128.0 * (double)ch * 2.0 / cu_rate);
-      if (e > 1) t += 2.0 * (double)e * (double)M * (double)N * 4.0 / 5.0e12 + 8e-6;
-      if (t < best * 0.999) {
-        best = t;
-        se = e;
-        chunk = ch;
-      }
-    }
+  } else {
+    forward_tile_plan(M, N, K, &fk, &se, &chunk);
   }
+  const int64_t tiles_m = cdiv(M, forward_tile_rows(fk)), tiles_n = cdiv(N, 128);
+  const int64_t tiles = tiles_m * tiles_n;
   const size_t part = se > 1 ? (size_t)se * (size_t)M * (size_t)N * sizeof(float) : 0;
   const size_t part_al = (part + 255) & ~(size_t)255;
   char* base = nullptr;
   hipError_t e = stream_workspace(stream, part_al + forward_frag_bytes(M, K), reinterpret_cast<void**>(&base));
   if (e != hipSuccess) return e;
   float* dst = se > 1 ? reinterpret_cast<float*>(base) : c;
-  e = launch_forward((int)(tiles * se), a, base + part_al, scales, reinterpret_cast<const uint32_t*>(codes), dst,
+  e = launch_forward(fk, (int)(tiles * se), a, base + part_al, scales, reinterpret_cast<const uint32_t*>(codes), dst,
                      (int)M, (int)N, (int)K, (int)chunk, (int)tiles_m, (int)tiles_n, stream);
   if (e != hipSuccess) return e;
   if (se > 1) {

@@ -272,13 +272,19 @@ int nf4_forward_grouped(const nf4_forward_problem* problems, int count, int64_t 
 /*
  * nf4_forward_forced -- nf4_forward with the kernel and the number of K
  * chunks forced, for tests and tuning: kernel NF4_FORWARD_TILE (512 x 128
- * tiles, any M) or NF4_FORWARD_STREAM (the streaming kernel nf4_forward picks
- * for 1 <= M <= 16; NF4_ERR_SHAPE for other M); `splits` >= 1, rounded so that
- * every chunk is a whole number of 64-wide blocks.  Same contract as
- * nf4_forward otherwise (the streaming kernel needs no fp16 copy of `a`).
+ * tiles, eight waves, any M), NF4_FORWARD_MID (256 x 128 tiles, four waves,
+ * two workgroups per CU), NF4_FORWARD_SMALL (128 x 128 tiles, four waves,
+ * three per CU) -- the three tile kernels give bitwise the same result for
+ * the same `splits` -- or NF4_FORWARD_STREAM (the streaming kernel
+ * nf4_forward picks for 1 <= M <= 16; NF4_ERR_SHAPE for other M); `splits`
+ * >= 1, rounded so that every chunk is a whole number of 64-wide blocks.
+ * Same contract as nf4_forward otherwise (the streaming kernel needs no fp16
+ * copy of `a`).
  */
 #define NF4_FORWARD_TILE 0
 #define NF4_FORWARD_STREAM 1
+#define NF4_FORWARD_MID 2
+#define NF4_FORWARD_SMALL 3
 int nf4_forward_forced(const float* a, const float* scales, const uint8_t* codes, float* c,
                        int64_t M, int64_t N, int64_t K, int kernel, int splits, hipStream_t stream);
 

@@ -72,7 +72,9 @@ def test_race_check_build_matches_release_grad_a(libs, kernel, rb, splits, M, N,
 
 
 @pytest.mark.parametrize("kernel,splits,M,N,K", [(0, 1, 600, 1024, 448), (0, 3, 1030, 520, 1088),
-                                                 (1, 1, 16, 2048, 1536), (1, 3, 5, 520, 1344)])
+                                                 (1, 1, 16, 2048, 1536), (1, 3, 5, 520, 1344),
+                                                 (2, 1, 600, 1024, 448), (2, 2, 257, 520, 640),
+                                                 (3, 1, 600, 1024, 448), (3, 3, 129, 264, 1088)])
 def test_race_check_build_matches_release_forward(libs, kernel, splits, M, N, K):
     rel, chk = libs
     _, s, b = _inputs(1, N, K, seed=M + N + K)

@@ -34,8 +34,8 @@ def fwd_inputs(M, N, K, seed):
     return a, s, b
 
 
-def check_forward(nb, a, s, b, M, N, K, splits=0, rows=None, what=""):
-    out = nb.forward(dev(a), dev(s), dev(b), splits=splits)
+def check_forward(nb, a, s, b, M, N, K, splits=0, rows=None, what="", kernel="auto"):
+    out = nb.forward(dev(a), dev(s), dev(b), splits=splits, kernel=kernel)
     gpu = host(out)
     if rows is not None:
         gpu = gpu[rows]
@@ -73,6 +73,21 @@ def test_forward_ragged_shapes(lib, M, N, K):
 def test_forward_split_k(lib, splits, M, N, K):
     a, s, b = fwd_inputs(M, N, K, seed=11 * M + N + K + splits)
     check_forward(lib, a, s, b, M, N, K, splits=splits, what=f"forward s{splits} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("kernel", ["mid", "small"])
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("M,N,K", [(17, 136, 192), (129, 256, 640), (300, 256, 1024), (700, 1000, 448),
+                                   (1030, 264, 1088)])
+def test_forward_mid_and_small_tiles(lib, kernel, splits, M, N, K):
+    """256 x 128 and 128 x 128 tiles (four waves, each lane doing two lanes' decode and table work of the
+    eight-wave kernel): ragged M around both tile heights, N past the last 128-column tile, K splits; within
+    the bound, the fp16-operand diagnostic, and bitwise equal to the 512 x 128 tiles with the same split."""
+    a, s, b = fwd_inputs(M, N, K, seed=5 * M + N + 3 * K + splits)
+    got = check_forward(lib, a, s, b, M, N, K, splits=splits, kernel=kernel,
+                        what=f"forward {kernel} s{splits} {M}x{N}x{K}")
+    ref = host(lib.forward(dev(a), dev(s), dev(b), splits=splits, kernel="tile"))
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
 def test_forward_attention_projection_config(lib):
@@ -163,7 +178,7 @@ def test_forward_one_hot_rows_give_fp16_weight_columns(lib):
     assert np.array_equal(gpu, w16[:, picks].T)
 
 
-@pytest.mark.parametrize("kernel", ["tile", "stream"])
+@pytest.mark.parametrize("kernel", ["tile", "mid", "small", "stream"])
 def test_forward_fp16_edge_values(lib, kernel):
     """Activations at RNE ties, fp16 subnormals, values rounding to zero and +-65504 against a single unit
     weight give fp16(a) exactly; one-hot activations against weights whose scales run from 1e-7 to 65000
