@@ -32,13 +32,15 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-# pairs of calls in a row, the second smaller: the streaming kernel with its in-kernel split sum (9, then
-# 8 N-chunks sharing the arrival counters), the fp32-fed wide kernel with 11 N-chunks of partials, the
-# fragment-fed wide kernel (fp16 A fragments in the scratch), and the fragment-fed kernel with split partials
+# pairs of calls in a row, the second smaller, over the kinds of plan nf4_grad_a makes: the streaming kernel
+# with its in-kernel split sum (9, then 8 N-chunks sharing the arrival counters); 256 x 128 tiles with fp16 A
+# fragments and 8 N-chunks of partials in the scratch, twice; 128 x 128 tiles unsplit (fragments only), then
+# 256 x 128 tiles unsplit; 256 x 128 tiles in 4 N-chunks, then 128 x 128 tiles unsplit
 SEQUENCES = [
     [(16, 18944, 3584), (4, 3000, 512)],
     [(600, 2048, 768), (100, 1024, 384)],
     [(2048, 1536, 1536), (1030, 256, 1088)],
+    [(1024, 3584, 3584), (300, 1024, 3584)],
 ]
 
 
