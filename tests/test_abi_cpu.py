@@ -117,3 +117,16 @@ def test_plan_is_consistent(nb, M, N, K):
         assert p["n_chunk"] % 64 == 0 and p["rb"] == 1
         bm, bk = {"mid": 256, "small": 128}.get(p["kernel"], 512), 128
         assert p["grid"] == -(-M // bm) * -(-K // bk) * p["splits"]
+
+
+@pytest.mark.parametrize("M,N,K,kernel,splits", [
+    (8192, 3584, 3584, "wide16", 1), (8192, 512, 3584, "mid", 1), (8192, 18944, 3584, "wide16", 1),
+    (8192, 3584, 18944, "wide16", 1), (2048, 1536, 1536, "small", 1), (4096, 8960, 1536, "wide16", 2),
+    (4096, 1536, 8960, "mid", 1), (1, 18944, 3584, "stream", 9), (16, 3584, 18944, "stream", 3)])
+def test_plan_choices_of_the_configurations(nb, M, N, K, kernel, splits):
+    """The plans measured fastest on MI355X for the benchmark's configurations (the full step's projections,
+    the attention projection, the MLP pair, the skinny sweep): a change of the cost model that moves one of
+    them has to be measured again."""
+    p = nb.grad_a_plan(M, N, K)
+    assert (p["kernel"], p["splits"]) == (kernel, splits), p
+
