@@ -262,7 +262,8 @@ def forward(a, scales, codes, out=None, stream=None, splits: int = 0, kernel: st
 
 def forward_grouped(problems, outs=None, stream=None):
     """Forward products of several problems sharing M in as few launches as possible (M <= 16: one grid of the
-    streaming kernel, each result bitwise that of forward()).
+    streaming kernel; larger M: problems with the same `a` tensor share one conversion of it), each result
+    bitwise that of forward().
 
     problems: sequence of (a [M, K], scales [N, K/64], codes [N, K/2]); returns the list of c [M, N] tensors
     (or fills `outs`)."""

@@ -341,6 +341,12 @@ hipError_t launch_forward(int kernel, int grid, const float* a, void* frags, con
                           int tiles_n, hipStream_t stream) {
   hipError_t e = launch_frag_pass(a, frags, M, K, /*natural=*/true, stream);
   if (e != hipSuccess) return e;
+  return launch_forward_tiles(kernel, grid, frags, scales, codes, dst, M, N, K, k_chunk, tiles_m, tiles_n, stream);
+}
+
+hipError_t launch_forward_tiles(int kernel, int grid, const void* frags, const float* scales, const uint32_t* codes,
+                                float* dst, int M, int N, int K, int k_chunk, int tiles_m, int tiles_n,
+                                hipStream_t stream) {
   if (kernel == kForwardMid)
     hipLaunchKernelGGL(nf4_forward_mid_kernel, dim3(grid), dim3(256), 0, stream, frags, scales, codes, dst, M, N, K,
                        k_chunk, tiles_m, tiles_n);

@@ -156,6 +156,10 @@ int forward_tile_rows(int kernel);
 hipError_t launch_forward(int kernel, int grid, const float* a, void* frags, const float* scales,
                           const uint32_t* codes, float* dst, int M, int N, int K, int k_chunk, int tiles_m,
                           int tiles_n, hipStream_t stream);
+// The tile kernel alone, on fragments a conversion pass already wrote.
+hipError_t launch_forward_tiles(int kernel, int grid, const void* frags, const float* scales, const uint32_t* codes,
+                                float* dst, int M, int N, int K, int k_chunk, int tiles_m, int tiles_n,
+                                hipStream_t stream);
 // Streaming forward kernel for M <= 16 (nf4_forward_skinny.hip): 128-column
 // strips (16 per wave) x K chunks of whole 128-wide steps.
 bool forward_stream_supported(int64_t M, int64_t N, int64_t K);

@@ -766,6 +766,8 @@ hipError_t launch_nf4_forward_grouped(const float* const* a, const float* const*
   int64_t se_of[kStreamGroupMax], chunk_of[kStreamGroupMax];
   int ng = 0;
   int64_t strips_split = 0;
+  int tiled[kStreamGroupMax];
+  int nt = 0;
   for (int i = 0; i < count; ++i) {
     if (N[i] == 0) continue;
     bool grouped = false;
@@ -782,8 +784,61 @@ hipError_t launch_nf4_forward_grouped(const float* const* a, const float* const*
       }
     }
     if (!grouped) {
-      hipError_t e = launch_nf4_forward(a[i], scales[i], codes[i], c[i], M, N[i], K[i], kForwardAuto, 0, stream);
+      if (K[i] > 0 && nt < kStreamGroupMax) {
+        tiled[nt++] = i;
+      } else {
+        hipError_t e = launch_nf4_forward(a[i], scales[i], codes[i], c[i], M, N[i], K[i], kForwardAuto, 0, stream);
+        if (e != hipSuccess) return e;
+      }
+    }
+  }
+  if (nt > 0) {
+    // Tile-kernel problems, each with the plan nf4_forward gives it.  Problems
+    // with the same activations (the same `a` and K, as q, k and v, or gate
+    // and up, of one layer) share one conversion of `a` into fp16 fragments.
+    // One workspace holds each distinct `a`'s fragments and the largest
+    // problem's split partials (the problems run in stream order, so they can
+    // reuse them), allocated before anything is launched.
+    int fk[kStreamGroupMax], src[kStreamGroupMax];
+    int64_t se[kStreamGroupMax], chunk[kStreamGroupMax];
+    size_t frag_off[kStreamGroupMax], frag_total = 0, part_max = 0;
+    for (int t = 0; t < nt; ++t) {
+      const int i = tiled[t];
+      forward_tile_plan(M, N[i], K[i], &fk[t], &se[t], &chunk[t]);
+      src[t] = t;
+      for (int u = 0; u < t; ++u)
+        if (a[tiled[u]] == a[i] && K[tiled[u]] == K[i]) {
+          src[t] = src[u];
+          break;
+        }
+      if (src[t] == t) {
+        frag_off[t] = frag_total;
+        frag_total += (forward_frag_bytes(M, K[i]) + 255) & ~(size_t)255;
+      }
+      if (se[t] > 1) part_max = std::max(part_max, (size_t)se[t] * (size_t)M * (size_t)N[i] * sizeof(float));
+    }
+    const size_t part_al = (part_max + 255) & ~(size_t)255;
+    char* base = nullptr;
+    hipError_t e = stream_workspace(stream, part_al + frag_total, reinterpret_cast<void**>(&base));
+    if (e != hipSuccess) return e;
+    for (int t = 0; t < nt; ++t) {
+      const int i = tiled[t];
+      void* frags = base + part_al + frag_off[src[t]];
+      if (src[t] == t) {
+        e = launch_frag_pass(a[i], frags, (int)M, (int)K[i], /*natural=*/true, stream);
+        if (e != hipSuccess) return e;
+      }
+      const int64_t tiles_m = cdiv(M, forward_tile_rows(fk[t])), tiles_n = cdiv(N[i], 128);
+      float* dst = se[t] > 1 ? reinterpret_cast<float*>(base) : c[i];
+      e = launch_forward_tiles(fk[t], (int)(tiles_m * tiles_n * se[t]), frags, scales[i],
+                               reinterpret_cast<const uint32_t*>(codes[i]), dst, (int)M, (int)N[i], (int)K[i],
+                               (int)chunk[t], (int)tiles_m, (int)tiles_n, stream);
       if (e != hipSuccess) return e;
+      if (se[t] > 1) {
+        const int64_t n4 = M * N[i] / 4;
+        e = launch_grad_a_reduce((int)std::min<int64_t>(cdiv(n4, 256), 8192), dst, c[i], n4, (int)se[t], stream);
+        if (e != hipSuccess) return e;
+      }
     }
   }
   if (ng == 0) return hipSuccess;

@@ -252,7 +252,10 @@ int nf4_forward(const float* a, const float* scales, const uint8_t* codes, float
  * streaming kernel runs in one grid of that kernel, each with its own plan's
  * strips and K-chunks, the largest chunks first; results are bitwise equal to
  * nf4_forward.  Any other problem (larger M, or limits of the in-kernel chunk
- * sum) runs as nf4_forward would run it.  Each problem's fields mean what
+ * sum) runs with the plan nf4_forward gives it, and problems among those with
+ * the same `a` pointer and K (a layer's q, k and v, or gate and up) share one
+ * conversion of `a` into fp16 fragments; results are again bitwise those of
+ * nf4_forward.  Each problem's fields mean what
  * nf4_forward's arguments mean, with the same layout, ownership, requirements
  * and bound; the c arrays must not alias each other or any input.  The chunk
  * partials share the stream's workspace.  NF4_ERR_SHAPE if count is outside

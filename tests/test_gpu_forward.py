@@ -333,6 +333,26 @@ def test_forward_grouped_matches_separate_calls(lib, M):
                 assert np.all(np.abs(gpu.astype(np.float64) - ref) <= 2e-3 * S + 1e-6), (M, N, K)
 
 
+def test_forward_grouped_shares_the_conversion_of_common_activations(lib):
+    """M > 16: problems with the same activations (q, k, v of a layer; gate and up) share one conversion of `a`
+    inside the grouped call; every result is bitwise that of its own nf4_forward call, including problems
+    whose plan splits K (partials reused between problems) and an unshared one in between."""
+    M = 600
+    x = dev(synth.grad_out_normal(M, 448, seed=81))
+    y = dev(synth.grad_out_normal(M, 320, seed=82))
+    ws = []
+    for j, (N, K) in enumerate([(512, 448), (128, 448), (128, 448), (264, 320), (1024, 448), (1024, 320)]):
+        _, s, b = fwd_inputs(1, N, K, seed=90 + j)
+        ws.append((dev(s), dev(b)))
+    problems = [(x,) + ws[0], (x,) + ws[1], (x,) + ws[2], (y,) + ws[3], (x,) + ws[4], (y,) + ws[5]]
+    outs = lib.forward_grouped(problems)
+    for p, o in zip(problems, outs):
+        ref = host(lib.forward(*p))
+        assert np.array_equal(host(o).view(np.uint32), ref.view(np.uint32))
+    a, s, b = host(x), host(ws[0][0]), host(ws[0][1])
+    check_forward(lib, a, s, b, M, 512, 448, what="grouped shared-a problem 0")
+
+
 def test_forward_grouped_large_m_and_errors(lib):
     """M > 16 problems run as nf4_forward runs them; more than 8 problems and mixed M are rejected."""
     M = 40
