@@ -205,28 +205,34 @@ __device__ __forceinline__ void stream_strip(const float* __restrict__ G, const 
     if (i < cnt) run_step(jj(i), s0);
   }
 
-  // fixed-order sum of the 8 waves: ((w0 + w1) + w2) + ... + w7
+  // fixed-order sum of the 8 waves: ((w0 + w1) + w2) + ... + w7, rows < M only
+  // (the padding rows' accumulators are zero and never stored)
   __syncthreads();
   {
     // accumulator lane (ci, q), register r: row 4q + r, columns 8ci + t
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const floatx4 lo = {acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
-      const floatx4 hi = {acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
-      lds_store_u32x4(smem, (uint32_t)((wave * 16 + 4 * q + r) * kSkinnyBK + 8 * ci) * 4u,
-                      __builtin_bit_cast(u32x4, lo));
-      lds_store_u32x4(smem, (uint32_t)((wave * 16 + 4 * q + r) * kSkinnyBK + 8 * ci + 4) * 4u,
-                      __builtin_bit_cast(u32x4, hi));
+      if (4 * q + r < M) {
+        const floatx4 lo = {acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+        const floatx4 hi = {acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
+        lds_store_u32x4(smem, (uint32_t)((wave * 16 + 4 * q + r) * kSkinnyBK + 8 * ci) * 4u,
+                        __builtin_bit_cast(u32x4, lo));
+        lds_store_u32x4(smem, (uint32_t)((wave * 16 + 4 * q + r) * kSkinnyBK + 8 * ci + 4) * 4u,
+                        __builtin_bit_cast(u32x4, hi));
+      }
     }
   }
   __syncthreads();
   {
     const int row = tid >> 5, c4 = tid & 31;  // 16 rows x 32 float4
-    floatx4 s = __builtin_bit_cast(floatx4, lds_load_u32x4(smem, (uint32_t)(row * kSkinnyBK + 4 * c4) * 4u));
+    floatx4 s = {0.f, 0.f, 0.f, 0.f};
+    if (row < M) {
+      s = __builtin_bit_cast(floatx4, lds_load_u32x4(smem, (uint32_t)(row * kSkinnyBK + 4 * c4) * 4u));
 #pragma unroll
-    for (int w = 1; w < kSkinnyWaves; ++w)
-      s += __builtin_bit_cast(floatx4,
-                              lds_load_u32x4(smem, (uint32_t)((w * 16 + row) * kSkinnyBK + 4 * c4) * 4u));
+      for (int w = 1; w < kSkinnyWaves; ++w)
+        s += __builtin_bit_cast(floatx4,
+                                lds_load_u32x4(smem, (uint32_t)((w * 16 + row) * kSkinnyBK + 4 * c4) * 4u));
+    }
     const int col = k0 + 4 * c4;
     const bool mine = row < M && col < K;
     const uint32_t at = 4u * ((uint32_t)row * (uint32_t)K + (uint32_t)col);  // byte offset in one partial
