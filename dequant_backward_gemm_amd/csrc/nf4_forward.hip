@@ -254,6 +254,9 @@ __device__ __forceinline__ void forward_tile(uint32_t* smem, const void* __restr
         if constexpr (t == 6 && s == 0) load_codes(st + 2, xn);
         if constexpr (t == 6 && s == 1) load_scales(st + 3, scn);
         if constexpr (t == 7 && s == 0) build_tables(sc, toff_build);
+        // (eight-wave tiles only: the four-wave ones, with two decode slots per
+        // lane, spill or run slower with the fixed order)
+        if constexpr (NW == 8) interleave_tick<RB>();
         __builtin_amdgcn_sched_barrier(0);
         NF4_PHASE_BARRIER();  // race-check build: every tick's LDS accesses complete before the next
       });

@@ -510,6 +510,10 @@ __device__ __forceinline__ void wide_tile(const void* __restrict__ Gv, const flo
           if constexpr (t == 6 && s == 0) load_codes(st + 2, xn);
           if constexpr (t == 6 && s == 1) load_scales(st + 3, scn);
           if constexpr (t == 7 && s == 0) build_tables(sc, toff_build);
+          // (not for the fp32-fed variant, whose registers do not fit the fixed
+          // order; the four-wave tiles, which hold two decode slots per lane,
+          // spill or run slower with it)
+          if constexpr (AF > 0) interleave_tick<4>();
         }
         __builtin_amdgcn_sched_barrier(0);
         NF4_PHASE_BARRIER();  // race-check build: every tick's LDS accesses complete before the next
