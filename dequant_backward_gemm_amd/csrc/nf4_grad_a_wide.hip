@@ -764,6 +764,7 @@ __device__ __forceinline__ void mid_tile(const void* __restrict__ Gv, const floa
         if constexpr (t == 6 && s == 0) load_codes(st + 2, xn);
         if constexpr (t == 6 && s == 1) load_scales(st + 3, scn);
         if constexpr (t == 7 && s == 0) build_tables(sc, toff_build);
+        if constexpr (RB == 4) interleave_tick_memory<RB>();
         __builtin_amdgcn_sched_barrier(0);
         NF4_PHASE_BARRIER();  // race-check build: every tick's LDS accesses complete before the next
       });
