@@ -784,7 +784,10 @@ hipError_t launch_nf4_forward_grouped(const float* const* a, const float* const*
       }
     }
     if (!grouped) {
-      if (K[i] > 0 && nt < kStreamGroupMax) {
+      // the problems nf4_forward runs on the tile kernels; the streaming ones
+      // left out of the group (limits of the in-kernel chunk sum) and K = 0
+      // run through nf4_forward's own launch
+      if (K[i] > 0 && !forward_stream_supported(M, N[i], K[i]) && nt < kStreamGroupMax) {
         tiled[nt++] = i;
       } else {
         hipError_t e = launch_nf4_forward(a[i], scales[i], codes[i], c[i], M, N[i], K[i], kForwardAuto, 0, stream);
