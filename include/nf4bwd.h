@@ -238,7 +238,8 @@ int nf4_grad_a_grouped(const nf4_grad_a_problem* problems, int count, int64_t M,
  *   2 GiB.  M == 0 or N == 0 enqueues nothing; K == 0 writes zeros.  Bitwise
  *   deterministic for a given (M, N, K).  1 <= M <= 16 runs a streaming
  *   kernel (256-column strips of C, the weight read once); larger M runs
- *   512 x 128 tiles.  Uses the stream's workspace (see the shared rules) for
+ *   512 x 128, 256 x 128 or 128 x 128 tiles, as the launch planner picks
+ *   for the shape.  Uses the stream's workspace (see the shared rules) for
  *   an fp16 copy of `a` (tiles: 2 * 16*ceil(M/16) * K bytes) and, when K is
  *   split, fp32 partials.
  */
