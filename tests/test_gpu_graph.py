@@ -73,10 +73,13 @@ def test_calls_in_a_graph_match_eager(lib):
             a_tile.copy_(torch.randn((300, 1024), device="cuda"))
             a_shared.copy_(torch.randn((200, 448), device="cuda"))
         st.synchronize()
-        graph.replay()
-        st.synchronize()
-        got = [o.clone() for o in outs + [c_fwd, c_tile] + grp_out + fgrp_out + tgrp_out]
+        # the replay, the copies of its results and the eager calls all on the capture stream: a replay
+        # uses that stream's workspace, so it must not overlap the eager calls
         with torch.cuda.stream(st):
+            graph.replay()
+        st.synchronize()
+        with torch.cuda.stream(st):
+            got = [o.clone() for o in outs + [c_fwd, c_tile] + grp_out + fgrp_out + tgrp_out]
             run()  # eager on the same inputs and workspace
         st.synchronize()
         want = outs + [c_fwd, c_tile] + grp_out + fgrp_out + tgrp_out
@@ -104,7 +107,8 @@ def test_capture_that_would_grow_the_workspace_is_refused(lib):
             raised = e
         x.add_(1.0)
     assert raised is not None and raised.status == lib.NF4_ERR_CAPTURE, raised
-    graph.replay()
+    with torch.cuda.stream(st):
+        graph.replay()
     st.synchronize()
     assert torch.equal(x, torch.ones(4, device="cuda"))
     with torch.cuda.stream(st):
@@ -116,6 +120,7 @@ def test_capture_that_would_grow_the_workspace_is_refused(lib):
     graph2 = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph2, stream=st):
         lib.grad_a_forced(g, s, b, "stream", rb=0, splits=4, out=o)
-    graph2.replay()
+    with torch.cuda.stream(st):
+        graph2.replay()
     st.synchronize()
     assert torch.equal(o.view(torch.int32), want.view(torch.int32))
