@@ -1,6 +1,10 @@
 """Seeded random shapes across every planner regime (M from 1 to ~1200, N ragged, K any multiple of 64):
 nf4_grad_a (default plan) and nf4_forward against the oracle, element by element, with the bound and the
-fp16-operand diagnostic; the plan taken is printed on failure."""
+fp16-operand diagnostic; the plan taken is printed on failure.  NF4_SHAPE_SEED (an integer) draws the
+same number of shapes from other seeds, for wider sweeps run by hand; the default seeds are the committed
+cases."""
+
+import os
 
 import numpy as np
 import pytest
@@ -28,7 +32,8 @@ def _shapes(count, seed):
     return out
 
 
-SHAPES = _shapes(36, seed=2024)
+_SEED = int(os.environ.get("NF4_SHAPE_SEED", "0"))
+SHAPES = _shapes(36, seed=2024 + 1000 * _SEED)
 
 
 def _tile_shapes(count, seed):
@@ -45,7 +50,7 @@ def _tile_shapes(count, seed):
     return out
 
 
-TILE_SHAPES = _tile_shapes(20, seed=2025)
+TILE_SHAPES = _tile_shapes(20, seed=2025 + 1000 * _SEED)
 
 
 def _check(gpu, ref, S, ref16, S16, red, what):
