@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -90,6 +91,21 @@ def test_validation_runs_before_any_device_work(nb):
                                    (4096, 8960, 1536), (4096, 1536, 8960), (8192, 512, 3584), (8192, 18944, 3584),
                                    (8192, 3584, 18944), (17, 100, 192), (3, 0, 64)])
 def test_plan_is_consistent(nb, M, N, K):
+    _check_plan(nb, M, N, K)
+
+
+def test_plan_is_consistent_on_random_shapes(nb):
+    """The same invariants over 2000 seeded random shapes, from skinny to the full step's sizes, N ragged or a
+    multiple of 64, K any multiple of 64 (host-only: the planner runs no device work)."""
+    rng = np.random.default_rng(77)
+    for _ in range(2000):
+        M = int(rng.choice([rng.integers(1, 17), rng.integers(17, 600), rng.integers(600, 9000)]))
+        N = int(rng.choice([rng.integers(0, 20000), 64 * rng.integers(1, 300)]))
+        K = 64 * int(rng.integers(1, 300))
+        _check_plan(nb, M, N, K)
+
+
+def _check_plan(nb, M, N, K):
     p = nb.grad_a_plan(M, N, K)
     if N == 0:
         assert p["kernel"] == "zero_fill"
