@@ -127,6 +127,30 @@ def test_pack_bit_exact(lib, N, K):
     assert np.array_equal(host(b), b_ref)
 
 
+def test_pack_weights_on_and_beside_the_thresholds(lib):
+    """Blocks whose weights sit on the fp32 values nearest to each decision threshold absmax * mid_i and on
+    their fp32 neighbours above and below, for absmax over the whole fp32 range (subnormal to 2^100) and both
+    signs of the absmax element: the codes must match the oracle's exact fp64 decision bit for bit."""
+    rng = np.random.default_rng(31)
+    q = oracle.NF4_LEVELS.astype(np.float64)
+    mids = (q[:-1] + q[1:]) / 2
+    N, K = 256, 128
+    w = np.zeros((N, K), dtype=np.float32)
+    for n in range(N):
+        for kb in range(K // 64):
+            a = np.float32(rng.uniform(1.0, 2.0) * 2.0 ** int(rng.integers(-140, 100)))
+            t = (np.float64(a) * mids).astype(np.float32)  # nearest fp32 (ties to even)
+            vals = np.concatenate([t, np.nextafter(t, np.float32(np.inf)), np.nextafter(t, np.float32(-np.inf))])
+            blk = rng.choice(vals, size=63)
+            lead = a if rng.random() < 0.5 else -a
+            w[n, 64 * kb:64 * kb + 64] = np.concatenate([[lead], blk]).astype(np.float32)
+    assert np.all(np.abs(w).reshape(N, -1, 64).max(axis=2) == np.abs(w[:, ::64]))
+    s, b = lib.pack(dev(w))
+    s_ref, b_ref = oracle.pack(w, N, K)
+    assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(host(b), b_ref)
+
+
 # ------------------------------------------------------------------- grad_A
 
 SMALL = [
