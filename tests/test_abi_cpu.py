@@ -146,3 +146,14 @@ def test_plan_choices_of_the_configurations(nb, M, N, K, kernel, splits):
     p = nb.grad_a_plan(M, N, K)
     assert (p["kernel"], p["splits"]) == (kernel, splits), p
 
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 exits with status 2 and says why, before touching any device."""
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(here, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr and r.stdout == ""
