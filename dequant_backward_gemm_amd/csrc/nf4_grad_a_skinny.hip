@@ -127,9 +127,14 @@ __device__ __forceinline__ void stream_strip(const float* __restrict__ G, const 
 
   auto run_step = [&](int j, const Step& d) {
     const int n0 = nb + 32 * j;
+    // Rows past the chunk can occur only in its last k-step: the row tests
+    // below run there only (the branch is uniform over the wave; skipping
+    // the selects in the other k-steps measured 0.2-0.9% faster).
+    const bool full = n0 + 32 <= ne;
     // tables of this k-step (rows past the chunk get scale 0)
     {
-      const float sc = (n0 + trow < ne) ? d.sc : 0.f;
+      float sc = d.sc;
+      if (!full) sc = (n0 + trow < ne) ? d.sc : 0.f;
       u32x4 w0, w1;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -145,8 +150,13 @@ __device__ __forceinline__ void stream_strip(const float* __restrict__ G, const 
     {
       const int nl = n0 + 8 * aq;
       float g[8];
+      if (full) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) g[i] = (nl + i < ne) ? d.a[i] : 0.f;
+        for (int i = 0; i < 8; ++i) g[i] = d.a[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) g[i] = (nl + i < ne) ? d.a[i] : 0.f;
+      }
       u32x4 h;
 #pragma unroll
       for (int p = 0; p < 4; ++p) h[p] = pack_half2_rne(g[2 * p], g[2 * p + 1]);
